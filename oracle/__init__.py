@@ -1,0 +1,256 @@
+"""fp64 CPU oracle of the quantized (W4A16) mixture-of-experts layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or execute
+this package: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it. It shares no code, table or constant with the HIP
+library (``bit_moe_expert_amd``) and imports nothing from it; it takes plain numpy
+arrays in the storage formats described below.
+
+What it computes, in the pages' order. The layer is the one the TensorFold issue
+"GB10: Nemotron decode is 1.4 % (code) / 3.0 % (prose) slower on 1.0.3 ..." (#627)
+describes in its Oct 14 comment on where the time per step goes: router -> topk ->
+plan -> routed experts, a shared expert beside them, then the weighted MoE add with
+the residual and a norm (``add_moe_norm``, table "Per-launch kernel times").
+The weights are NVFP4 read as W4A16: 4-bit float weights with scales, computed
+against BF16 activations (bear-blog article on TensorFold 1.0.12 / PR804, section
+"NVFP4 is neither uniform 4-bit nor all-FP4 compute"). The issue's maintainers gate
+their kernels on the error against a 64-bit reference (#627, description and the
+Oct 10 reply); this oracle is such a reference.
+
+Readings where the pages are silent (each is stated again where it is used):
+  R1  E2M1 = 1 sign, 2 exponent bits (bias 1), 1 mantissa bit; OCP MX v1.0.
+  R2  the block scale is OCP FP8 E4M3FN (bias 7, no infinities, 0x7F/0xFF NaN).
+  R3  weight = e2m1(code) * e4m3(block scale) * fp32 tensor scale.
+  R4  16-weight blocks run along K (the reduction axis); element 2j is the low nibble.
+  R5  W13 rows 0..I-1 are the gate, rows I..2I-1 the up projection; SwiGLU
+      h = silu(gate) * up (Shazeer, "GLU Variants Improve Transformer", 2020).
+  R6  routing weights = softmax over all experts, top-k selected, renormalised.
+  R7  top-k order: larger logit first; equal logits -> lower expert index first.
+  R8  the plan (permutation) is the stable counting sort of the flat pair index
+      f = t*k + j by expert.
+  R9  the shared expert is ungated (weight 1) and sees every token.
+  R10 RMSNorm n = o / sqrt(mean(o^2) + eps) * gamma (Zhang & Sennrich, 2019), with
+      o = residual + sum_j w_j * y_j (+ shared); both o and n are layer outputs.
+  R11 intermediates are not rounded here (fp64 throughout).
+
+Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
+(closed forms, library routines, brute force on tiny inputs, invariants).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_value", "e2m1_value", "e4m3_value", "unpack_codes", "dequant",
+    "router_logits", "route", "permute", "swiglu_ffn", "expert_outputs",
+    "combine_norm", "layer",
+]
+
+
+# ----------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns (uint16) -> fp64. BF16 is the top half of an IEEE binary32."""
+    b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def e2m1_value(code: np.ndarray) -> np.ndarray:
+    """4-bit E2M1 code -> fp64 (reading R1).
+
+    Bits s e1 e0 m: exponent field 0 is subnormal (0.5*m), otherwise
+    2^(e-1) * (1 + m/2); the sign bit negates (code 8 is -0).
+    """
+    c = np.asarray(code).astype(np.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int64)))
+    return np.where(s == 1, -mag, mag)
+
+
+def e4m3_value(code: np.ndarray) -> np.ndarray:
+    """8-bit OCP E4M3FN code -> fp64 (reading R2).
+
+    Bits s e3..e0 m2..m0, bias 7: exponent field 0 is subnormal 2^-6 * m/8,
+    otherwise 2^(e-7) * (1 + m/8); e=15, m=7 is NaN; there is no infinity.
+    """
+    c = np.asarray(code).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64)))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    """[..., K/2] bytes -> [..., K] 4-bit codes; element 2j is the low nibble (R4)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0x0F
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def dequant(packed: np.ndarray, scales: np.ndarray, tscale: float) -> np.ndarray:
+    """One expert's 4-bit matrix -> fp64 [N, K] (reading R3).
+
+    ``packed`` is [N, K/2], ``scales`` [N, K/16] E4M3 codes, ``tscale`` the FP32
+    tensor scale; weight[n, k] = e2m1(code[n, k]) * e4m3(scales[n, k // 16]) * tscale.
+    """
+    codes = unpack_codes(packed)
+    block = np.repeat(e4m3_value(scales), 16, axis=-1)
+    return e2m1_value(codes) * block * float(tscale)
+
+
+# ----------------------------------------------------------------------------
+# Router, top-k and the plan (issue #627, Oct 14 comment: router -> topk -> plan)
+# ----------------------------------------------------------------------------
+def router_logits(x_bits: np.ndarray, wr_bits: np.ndarray) -> np.ndarray:
+    """logits[t, e] = sum_h x[t, h] * Wr[e, h], BF16 operands, fp64 sums."""
+    return bf16_value(x_bits) @ bf16_value(wr_bits).T
+
+
+def route(logits: np.ndarray, k: int):
+    """Top-k experts per token and their weights (readings R6, R7).
+
+    Softmax over all E logits, then the k largest (ties -> lower index), then the
+    selected probabilities renormalised to sum to 1. Returns (idx int32 [T,k],
+    w fp64 [T,k]) with idx in selection order.
+    """
+    L = np.asarray(logits, dtype=np.float64)
+    T, E = L.shape
+    p = np.exp(L - L.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    idx = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    for t in range(T):
+        # sort key: larger logit first, then lower expert index
+        order = sorted(range(E), key=lambda e: (-L[t, e], e))[:k]
+        idx[t] = order
+        sel = p[t, order]
+        w[t] = sel / sel.sum()
+    return idx, w
+
+
+def permute(idx: np.ndarray, E: int):
+    """The routing plan (reading R8).
+
+    Flat pair f = t*k + j goes to expert idx[t, j]. offsets[e] = number of pairs of
+    experts < e; perm_src lists, expert by expert, the flat indices f of that
+    expert in ascending order; inv[f] is the position of f in perm_src.
+    """
+    flat = np.asarray(idx).reshape(-1)
+    counts = np.zeros(E, dtype=np.int64)
+    for e in flat:
+        counts[e] += 1
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    perm_src = np.concatenate(
+        [np.flatnonzero(flat == e) for e in range(E)] + [np.zeros(0, dtype=np.int64)]
+    ).astype(np.int32)
+    inv = np.empty(flat.size, dtype=np.int32)
+    inv[perm_src] = np.arange(flat.size, dtype=np.int32)
+    return offsets, perm_src, inv
+
+
+# ----------------------------------------------------------------------------
+# Expert FFN (W4A16 SwiGLU), reading R5
+# ----------------------------------------------------------------------------
+def swiglu_ffn(x: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """y = W2 (silu(Wg x) * (Wu x)) for each row of x (fp64).
+
+    x [R, H]; w13 [2I, H] (gate rows first, then up rows); w2 [H, I].
+    """
+    I = w13.shape[0] // 2
+    g = x @ w13[:I].T
+    u = x @ w13[I:].T
+    a = g / (1.0 + np.exp(-g)) * u
+    return a @ w2.T
+
+
+def expert_outputs(x_bits, idx, w13, w2, tokens=None, cache=None) -> np.ndarray:
+    """y[t, j] = FFN_{idx[t, j]}(x[t]) for the selected tokens (fp64 [len(tokens), k, H]).
+
+    ``w13``/``w2`` are objects with ``packed``, ``scales`` and ``tscale`` arrays
+    over experts. Experts are dequantised one at a time; ``cache`` (a dict) may keep
+    them between calls.
+    """
+    idx = np.asarray(idx)
+    tokens = np.arange(idx.shape[0]) if tokens is None else np.asarray(tokens)
+    x = bf16_value(np.asarray(x_bits)[tokens])
+    sel = idx[tokens]
+    k = sel.shape[1]
+    H = x.shape[1]
+    y = np.zeros((len(tokens), k, H), dtype=np.float64)
+    for e in np.unique(sel):
+        rr, jj = np.nonzero(sel == e)
+        W13, W2 = _expert(w13, w2, int(e), cache)
+        y[rr, jj] = swiglu_ffn(x[rr], W13, W2)
+    return y
+
+
+def _expert(w13, w2, e, cache):
+    if cache is not None and e in cache:
+        return cache[e]
+    W13 = dequant(w13.packed[e], w13.scales[e], w13.tscale[e])
+    W2 = dequant(w2.packed[e], w2.scales[e], w2.tscale[e])
+    if cache is not None:
+        cache[e] = (W13, W2)
+    return W13, W2
+
+
+# ----------------------------------------------------------------------------
+# Weighted combine, residual add and RMSNorm (add_moe_norm), readings R9, R10
+# ----------------------------------------------------------------------------
+def combine_norm(y, w, residual_bits, gamma_bits, eps, shared=None):
+    """o = residual + sum_j w[t,j] * y[t,j] (+ shared[t]); n = o / rms(o) * gamma.
+
+    y fp64 [T, k, H], w [T, k]; returns (o, n) in fp64.
+    """
+    o = bf16_value(residual_bits) + np.einsum("tj,tjh->th", np.asarray(w, np.float64), y)
+    if shared is not None:
+        o = o + shared
+    ms = np.mean(o * o, axis=1, keepdims=True)
+    n = o / np.sqrt(ms + eps) * bf16_value(gamma_bits)[None, :]
+    return o, n
+
+
+# ----------------------------------------------------------------------------
+# Whole layer
+# ----------------------------------------------------------------------------
+def layer(inp, tokens=None, cache=None, logits=None):
+    """The whole layer for one call's inputs (an object with the fields of
+    ``LayerInputs``: x, residual, gamma, w13, w2, logits or w_router, shared13,
+    shared2, w.k, w.E, w.eps).
+
+    With ``tokens`` only those rows are computed (routing, FFN, combine and norm are
+    per token, so a subset is exact); the plan is then left out. ``logits``
+    overrides the router (for reusing the fp64 logits of a previous call).
+    Returns a dict of fp64 / int32 arrays.
+    """
+    wl = inp.w
+    T = inp.x.shape[0]
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    if logits is None:
+        if inp.logits is not None:
+            logits = np.asarray(inp.logits, dtype=np.float64)[tok]
+        else:
+            logits = router_logits(np.asarray(inp.x)[tok], inp.w_router)
+    idx, w = route(logits, wl.k)
+    full_idx = np.zeros((T, wl.k), dtype=np.int32)
+    full_idx[tok] = idx
+    y = expert_outputs(inp.x, full_idx, inp.w13, inp.w2, tokens=tok, cache=cache)
+    shared = None
+    if getattr(inp, "shared13", None) is not None:
+        W13 = dequant(inp.shared13.packed[0], inp.shared13.scales[0], inp.shared13.tscale[0])
+        W2 = dequant(inp.shared2.packed[0], inp.shared2.scales[0], inp.shared2.tscale[0])
+        shared = swiglu_ffn(bf16_value(np.asarray(inp.x)[tok]), W13, W2)
+    o, n = combine_norm(y, w, np.asarray(inp.residual)[tok], inp.gamma, wl.eps, shared)
+    out = {"logits": logits, "idx": idx, "w": w, "y": y, "o": o, "n": n, "tokens": tok}
+    if tokens is None:
+        out["offsets"], out["perm_src"], out["inv"] = permute(idx, wl.E)
+    return out

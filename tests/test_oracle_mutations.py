@@ -1,0 +1,148 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in the oracle (monkeypatching a function of the
+``oracle`` module, so the other oracle functions see it too) and checks that at
+least one of the pins in ``test_oracle_pins`` then fails.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+_orig = {name: getattr(oracle, name) for name in oracle.__all__}
+
+
+def _e2m1_bias0(code):  # exponent bias 0 instead of 1
+    return _orig["e2m1_value"](code) * 2.0
+
+
+def _e4m3_bias8(code):  # the FNUZ exponent bias
+    return _orig["e4m3_value"](code) / 2.0
+
+
+def _unpack_high_first(packed):
+    c = _orig["unpack_codes"](packed)
+    out = c.copy()
+    out[..., 0::2], out[..., 1::2] = c[..., 1::2], c[..., 0::2]
+    return out
+
+
+def _dequant_block32(packed, scales, tscale):  # scales applied per 32 instead of per 16
+    codes = oracle.unpack_codes(packed)
+    block = np.repeat(oracle.e4m3_value(scales), 32, axis=-1)[..., : codes.shape[-1]]
+    return oracle.e2m1_value(codes) * block * float(tscale)
+
+
+def _dequant_no_tscale(packed, scales, tscale):
+    return _orig["dequant"](packed, scales, 1.0)
+
+
+def _router_drop_last_term(x_bits, wr_bits):
+    return oracle.bf16_value(x_bits)[:, :-1] @ oracle.bf16_value(wr_bits)[:, :-1].T
+
+
+def _route_no_renorm(logits, k):
+    idx, _ = _orig["route"](logits, k)
+    L = np.asarray(logits, dtype=np.float64)
+    p = np.exp(L - L.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    return idx, np.take_along_axis(p, idx.astype(np.int64), 1)
+
+
+def _route_ties_high(logits, k):
+    L = np.asarray(logits, dtype=np.float64)
+    idx, w = _orig["route"](L[:, ::-1], k)
+    return (L.shape[1] - 1 - idx).astype(np.int32), w
+
+
+def _permute_unstable(idx, E):
+    offsets, perm, inv = _orig["permute"](idx, E)
+    perm = perm.copy()
+    for e in range(E):
+        perm[offsets[e]:offsets[e + 1]] = perm[offsets[e]:offsets[e + 1]][::-1]
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size, dtype=np.int32)
+    return offsets, perm, inv
+
+
+def _swiglu_swapped(x, w13, w2):
+    I = w13.shape[0] // 2
+    return _orig["swiglu_ffn"](x, np.concatenate([w13[I:], w13[:I]]), w2)
+
+
+def _swiglu_w2_transposed_use(x, w13, w2):
+    I = w13.shape[0] // 2
+    g = x @ w13[:I].T
+    u = x @ w13[I:].T
+    a = g / (1.0 + np.exp(-g)) * u
+    return a @ w2[:, ::-1].T  # columns of W2 in the wrong order
+
+
+def _combine_no_residual(y, w, residual_bits, gamma_bits, eps, shared=None):
+    return _orig["combine_norm"](y, w, np.zeros_like(residual_bits), gamma_bits, eps, shared)
+
+
+def _combine_no_gamma(y, w, residual_bits, gamma_bits, eps, shared=None):
+    ones = np.full_like(gamma_bits, 0x3F80)
+    return _orig["combine_norm"](y, w, residual_bits, ones, eps, shared)
+
+
+def _combine_shared_dropped(y, w, residual_bits, gamma_bits, eps, shared=None):
+    return _orig["combine_norm"](y, w, residual_bits, gamma_bits, eps, None)
+
+
+MUTANTS = {
+    "e2m1_value": [_e2m1_bias0],
+    "e4m3_value": [_e4m3_bias8],
+    "unpack_codes": [_unpack_high_first],
+    "dequant": [_dequant_block32, _dequant_no_tscale],
+    "router_logits": [_router_drop_last_term],
+    "route": [_route_no_renorm, _route_ties_high],
+    "permute": [_permute_unstable],
+    "swiglu_ffn": [_swiglu_swapped, _swiglu_w2_transposed_use],
+    "combine_norm": [_combine_no_residual, _combine_no_gamma, _combine_shared_dropped],
+}
+
+CASES = [(name, fn) for name, fns in MUTANTS.items() for fn in fns]
+
+
+def _all_pins():
+    out = []
+    for name in dir(pins):
+        if not name.startswith("test_"):
+            continue
+        fn = getattr(pins, name)
+        marks = getattr(fn, "pytestmark", [])
+        params = [m for m in marks if m.name == "parametrize"]
+        if params:
+            argnames, values = params[0].args[0], params[0].args[1]
+            argnames = [a.strip() for a in argnames.split(",")]
+            for v in values:
+                v = v if isinstance(v, tuple) else (v,)
+                out.append((name, fn, dict(zip(argnames, v))))
+        else:
+            out.append((name, fn, {}))
+    return out
+
+
+@pytest.mark.parametrize("target,mutant", CASES, ids=[f"{n}:{f.__name__}" for n, f in CASES])
+def test_pins_catch_planted_mistake(target, mutant, monkeypatch):
+    monkeypatch.setattr(oracle, target, mutant)
+    caught = []
+    for name, fn, kwargs in _all_pins():
+        try:
+            fn(**kwargs)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(name)
+    assert caught, f"no pin fails with {target} replaced by {mutant.__name__}"
+
+
+def test_pins_pass_without_mutation():
+    failed = []
+    for name, fn, kwargs in _all_pins():
+        try:
+            fn(**kwargs)
+        except AssertionError:
+            failed.append(name)
+    assert not failed

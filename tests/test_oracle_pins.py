@@ -1,0 +1,310 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each test checks one oracle function against a published table, a library routine,
+a closed form, an invariant, or a brute-force computation written independently
+(pure-Python loops / exact rationals) on tiny inputs.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_moe_expert_amd import workloads as wl
+from tests.conftest import read_golden
+
+
+# ----------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------
+def test_e2m1_all_codes_match_ocp_table():
+    rows = read_golden("e2m1_values.txt")
+    codes = np.array([c for c, _ in rows])
+    want = np.array([v for _, v in rows])
+    got = oracle.e2m1_value(codes)
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))  # code 8 is -0
+
+
+def test_e4m3_all_codes_match_torch_float8():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_value(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_e4m3_landmarks_match_ofp8_spec():
+    for code, val in read_golden("e4m3_landmarks.txt"):
+        got = float(oracle.e4m3_value(np.array([code]))[0])
+        if math.isnan(val):
+            assert math.isnan(got)
+        else:
+            assert got == val and math.copysign(1, got) == math.copysign(1, val), hex(code)
+
+
+def test_bf16_value_matches_torch():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 1 << 16, 4096).astype(np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]  # finite values only
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.bf16_value(bits), ref)
+
+
+def test_unpack_codes_low_nibble_first():
+    rng = np.random.default_rng(2)
+    codes = rng.integers(0, 16, (3, 64)).astype(np.uint8)
+    packed = np.zeros((3, 32), dtype=np.uint8)
+    for r in range(3):
+        for j in range(32):
+            packed[r, j] = int(codes[r, 2 * j]) + 16 * int(codes[r, 2 * j + 1])
+    assert np.array_equal(oracle.unpack_codes(packed), codes)
+
+
+def test_dequant_matches_elementwise_definition_and_is_exact_in_bf16():
+    rng = np.random.default_rng(3)
+    N, K = 5, 64
+    packed = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    scales = wl.to_e4m3_codes(np.exp2(rng.uniform(-4, 2, (N, K // 16))))
+    ts = 0.5
+    W = oracle.dequant(packed, scales, ts)
+    e2m1 = dict(read_golden("e2m1_values.txt"))
+    sc = torch.from_numpy(scales).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for n in range(N):
+        for k in range(K):
+            byte = int(packed[n, k // 2])
+            code = byte & 15 if k % 2 == 0 else byte >> 4
+            assert W[n, k] == e2m1[code] * sc[n, k // 16] * ts
+    # code * scale has <= 6 significant bits: BF16 holds it exactly
+    bf = torch.from_numpy(W).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(bf, W)
+
+
+def test_dequant_full_e4m3_range_products_exact_in_bf16():
+    # every (code, scale) pair of the formats, tensor scale 1
+    codes = np.arange(16)
+    scales = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    prod = oracle.e2m1_value(codes)[:, None] * oracle.e4m3_value(scales)[None, :]
+    bf = torch.from_numpy(prod).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(bf, prod)
+
+
+# ----------------------------------------------------------------------------
+# Router, top-k, plan
+# ----------------------------------------------------------------------------
+def test_router_logits_brute_force_exact():
+    rng = np.random.default_rng(4)
+    T, E, H = 3, 4, 16
+    x = wl.to_bf16_bits(rng.standard_normal((T, H)))
+    wr = wl.to_bf16_bits(rng.standard_normal((E, H)) * 0.02)
+    got = oracle.router_logits(x, wr)
+    xf = oracle.bf16_value(x)
+    wf = oracle.bf16_value(wr)
+    for t in range(T):
+        for e in range(E):
+            exact = sum(Fraction(float(xf[t, h])) * Fraction(float(wf[e, h])) for h in range(H))
+            assert abs(Fraction(float(got[t, e])) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+
+
+def _margin_logits(T, E, k, seed):
+    w = wl.Workload("t", T=T, H=128, E=E, k=k, I=128, routing="normal", margin=1e-3)
+    return wl._draw_logits(np.random.SeedSequence(seed), w, T)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (128, 8), (160, 8), (256, 8), (7, 7), (5, 1)])
+def test_route_matches_torch_topk_and_softmax(E, k):
+    L = _margin_logits(64, E, k, seed=E * 31 + k)
+    idx, w = oracle.route(L, k)
+    tl = torch.from_numpy(L.astype(np.float64))
+    vals, ti = torch.topk(tl, k, dim=1, largest=True, sorted=True)
+    assert np.array_equal(idx, ti.numpy().astype(np.int32))
+    ref_w = torch.softmax(vals, dim=1).numpy()
+    np.testing.assert_allclose(w, ref_w, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+
+
+def test_route_k_equals_e_is_full_softmax_and_k1_is_one():
+    L = _margin_logits(16, 6, 5, seed=9)
+    idx, w = oracle.route(L, 6)
+    full = torch.softmax(torch.from_numpy(L.astype(np.float64)), dim=1).numpy()
+    np.testing.assert_allclose(w, np.take_along_axis(full, idx.astype(np.int64), 1), rtol=1e-13)
+    idx1, w1 = oracle.route(L, 1)
+    assert np.all(w1 == 1.0)
+    assert np.array_equal(idx1[:, 0], np.argmax(L, axis=1))
+
+
+def test_route_ties_go_to_lower_index():
+    L = np.array([[1.0, 3.0, 3.0, 0.5, 3.0, 2.0]])
+    idx, w = oracle.route(L, 4)
+    assert idx.tolist() == [[1, 2, 4, 5]]
+    np.testing.assert_allclose(w[0, :3], w[0, 0])
+
+
+@pytest.mark.parametrize("T,k,E,mode", [(64, 8, 128, "uniform"), (16, 2, 8, "uniform"),
+                                        (40, 4, 16, "one_hot_expert"), (1, 8, 128, "uniform"),
+                                        (12, 6, 6, "all_experts"), (30, 2, 64, "sparse")])
+def test_permute_matches_stable_argsort(T, k, E, mode):
+    rng = np.random.default_rng(T * k + E)
+    if mode == "one_hot_expert":
+        idx = np.full((T, k), 3, dtype=np.int32)
+        idx[:, 1:] = rng.integers(0, E, (T, k - 1))
+    elif mode == "all_experts":
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    elif mode == "sparse":
+        idx = rng.choice([5, 9, 63], (T, k)).astype(np.int32)
+    else:
+        idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    offsets, perm, inv = oracle.permute(idx, E)
+    flat = idx.reshape(-1)
+    assert np.array_equal(perm, np.argsort(flat, kind="stable").astype(np.int32))
+    assert np.array_equal(np.diff(offsets), np.bincount(flat, minlength=E))
+    assert offsets[0] == 0 and offsets[-1] == flat.size
+    assert np.array_equal(perm[inv], np.arange(flat.size))   # perm o inv = id
+    assert np.array_equal(inv[perm], np.arange(flat.size))   # inv o perm = id
+    assert np.array_equal(flat[perm], np.sort(flat, kind="stable"))
+
+
+def test_permute_empty():
+    offsets, perm, inv = oracle.permute(np.zeros((0, 4), dtype=np.int32), 8)
+    assert offsets.tolist() == [0] * 9 and perm.size == 0 and inv.size == 0
+
+
+# ----------------------------------------------------------------------------
+# Expert FFN
+# ----------------------------------------------------------------------------
+def _brute_swiglu(x, w13, w2):
+    """Pure-Python loops, math.exp: independent of numpy's matmul."""
+    R, H = x.shape
+    I = w13.shape[0] // 2
+    out = np.zeros((R, w2.shape[0]))
+    for r in range(R):
+        a = []
+        for i in range(I):
+            g = math.fsum(float(x[r, h]) * float(w13[i, h]) for h in range(H))
+            u = math.fsum(float(x[r, h]) * float(w13[I + i, h]) for h in range(H))
+            a.append(g / (1.0 + math.exp(-g)) * u)
+        for n in range(w2.shape[0]):
+            out[r, n] = math.fsum(float(w2[n, i]) * a[i] for i in range(I))
+    return out
+
+
+def test_swiglu_ffn_brute_force():
+    rng = np.random.default_rng(5)
+    R, H, I = 3, 32, 16
+    x = oracle.bf16_value(wl.to_bf16_bits(rng.standard_normal((R, H))))
+    w13 = oracle.dequant(rng.integers(0, 256, (2 * I, H // 2)).astype(np.uint8),
+                         wl.to_e4m3_codes(np.exp2(rng.uniform(-4, 2, (2 * I, H // 16)))), 1.0)
+    w2 = oracle.dequant(rng.integers(0, 256, (H, I // 2)).astype(np.uint8),
+                        wl.to_e4m3_codes(np.exp2(rng.uniform(-4, 2, (H, I // 16)))), 1.0)
+    np.testing.assert_allclose(oracle.swiglu_ffn(x, w13, w2), _brute_swiglu(x, w13, w2), rtol=1e-11, atol=1e-9)
+
+
+def test_e1_k1_layer_is_a_dense_swiglu_mlp_via_torch():
+    """E=1, k=1: every token goes to the one expert with weight 1; the layer is a
+    dense SwiGLU MLP + residual + RMSNorm, computed here with torch library ops on
+    weights decoded through torch's float8 type and the OCP E2M1 table."""
+    w = wl.Workload("dense", T=6, H=128, E=1, k=1, I=128, routing="normal")
+    inp = wl.make_inputs(w, seed=11)
+    out = oracle.layer(inp)
+    assert np.all(out["idx"] == 0) and np.all(out["w"] == 1.0)
+    e2m1 = torch.tensor([v for _, v in read_golden("e2m1_values.txt")], dtype=torch.float64)
+
+    def deq(m):
+        p = torch.from_numpy(m.packed[0].astype(np.int64))
+        codes = torch.stack([p & 15, p >> 4], dim=-1).reshape(p.shape[0], -1)
+        sc = torch.from_numpy(m.scales[0]).view(torch.float8_e4m3fn).to(torch.float64)
+        return e2m1[codes] * sc.repeat_interleave(16, dim=1) * float(m.tscale[0])
+
+    x = torch.from_numpy(inp.x.view(np.int16)).view(torch.bfloat16).double()
+    r = torch.from_numpy(inp.residual.view(np.int16)).view(torch.bfloat16).double()
+    g = torch.from_numpy(inp.gamma.view(np.int16)).view(torch.bfloat16).double()
+    W13, W2 = deq(inp.w13), deq(inp.w2)
+    I = w.I
+    hmid = torch.nn.functional.silu(x @ W13[:I].T) * (x @ W13[I:].T)
+    o = r + hmid @ W2.T
+    n = torch.nn.functional.rms_norm(o, (w.H,), weight=g, eps=w.eps)
+    np.testing.assert_allclose(out["o"], o.numpy(), rtol=1e-12, atol=1e-10)
+    np.testing.assert_allclose(out["n"], n.numpy(), rtol=1e-12, atol=1e-10)
+
+
+def test_expert_outputs_equal_per_token_loop():
+    w = wl.workload("tiny")
+    inp = wl.make_inputs(w, seed=0)
+    idx, _ = oracle.route(inp.logits, w.k)
+    y = oracle.expert_outputs(inp.x, idx, inp.w13, inp.w2)
+    x = oracle.bf16_value(inp.x)
+    for t in (0, 5, 15):
+        for j in range(w.k):
+            e = int(idx[t, j])
+            W13 = oracle.dequant(inp.w13.packed[e], inp.w13.scales[e], inp.w13.tscale[e])
+            W2 = oracle.dequant(inp.w2.packed[e], inp.w2.scales[e], inp.w2.tscale[e])
+            np.testing.assert_allclose(y[t, j], oracle.swiglu_ffn(x[t:t + 1], W13, W2)[0], rtol=1e-11)
+
+
+# ----------------------------------------------------------------------------
+# Combine + RMSNorm
+# ----------------------------------------------------------------------------
+def test_combine_norm_matches_torch_rms_norm():
+    rng = np.random.default_rng(6)
+    T, k, H = 5, 3, 64
+    y = rng.standard_normal((T, k, H))
+    w = rng.random((T, k))
+    res = wl.to_bf16_bits(rng.standard_normal((T, H)))
+    gam = wl.to_bf16_bits(rng.uniform(0.5, 1.5, H))
+    sh = rng.standard_normal((T, H))
+    o, n = oracle.combine_norm(y, w, res, gam, 1e-6, shared=sh)
+    o_ref = oracle.bf16_value(res) + sum(w[:, j:j + 1] * y[:, j] for j in range(k)) + sh
+    np.testing.assert_allclose(o, o_ref, rtol=1e-14, atol=1e-14)
+    n_ref = torch.nn.functional.rms_norm(torch.from_numpy(o_ref), (H,),
+                                         weight=torch.from_numpy(oracle.bf16_value(gam)), eps=1e-6)
+    np.testing.assert_allclose(n, n_ref.numpy(), rtol=1e-13, atol=1e-14)
+
+
+def test_combine_norm_closed_forms():
+    rng = np.random.default_rng(7)
+    T, k, H = 4, 2, 128
+    res = wl.to_bf16_bits(rng.standard_normal((T, H)))
+    ones = wl.to_bf16_bits(np.ones(H))
+    r = oracle.bf16_value(res)
+    # y = 0: o = r, n = r / rms(r)
+    o, n = oracle.combine_norm(np.zeros((T, k, H)), np.full((T, k), 0.5), res, ones, 1e-12)
+    np.testing.assert_array_equal(o, r)
+    np.testing.assert_allclose(n, r / np.sqrt(np.mean(r * r, axis=1, keepdims=True)), rtol=1e-12)
+    # gamma = 1: rms(n) = 1 (eps small against mean square)
+    np.testing.assert_allclose(np.sqrt(np.mean(n * n, axis=1)), 1.0, rtol=1e-10)
+    # scale invariance of the norm: n(c * o) = n(o) for c = 4 (exact power of two)
+    y = rng.standard_normal((T, k, H))
+    w = rng.random((T, k))
+    _, n1 = oracle.combine_norm(y, w, res, ones, 1e-30)
+    res4 = wl.to_bf16_bits(4 * r)
+    _, n4 = oracle.combine_norm(4 * y, w, res4, ones, 1e-30)
+    np.testing.assert_allclose(n4, n1, rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# Whole layer: per-token independence
+# ----------------------------------------------------------------------------
+def test_layer_rows_are_independent_of_batch():
+    w = wl.workload("tiny")
+    inp = wl.make_inputs(w, seed=0)
+    full = oracle.layer(inp)
+    sub = oracle.layer(inp, tokens=np.array([3, 7, 11]))
+    np.testing.assert_array_equal(sub["idx"], full["idx"][[3, 7, 11]])
+    # equal up to the rounding order of the library matmul
+    np.testing.assert_allclose(sub["o"], full["o"][[3, 7, 11]], rtol=1e-11)
+    np.testing.assert_allclose(sub["n"], full["n"][[3, 7, 11]], rtol=1e-11)
+
+
+def test_layer_composition_matches_steps():
+    w = wl.workload("tiny")
+    inp = wl.make_inputs(w, seed=0)
+    out = oracle.layer(inp)
+    offsets, perm, inv = oracle.permute(out["idx"], w.E)
+    assert np.array_equal(out["perm_src"], perm) and np.array_equal(out["inv"], inv)
+    assert np.array_equal(out["offsets"], offsets)
+    np.testing.assert_allclose(out["w"].sum(axis=1), 1.0, atol=1e-14)

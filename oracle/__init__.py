@@ -31,7 +31,10 @@ Readings where the pages are silent (each is stated again where it is used):
   R9  the shared expert is ungated (weight 1) and sees every token.
   R10 RMSNorm n = o / sqrt(mean(o^2) + eps) * gamma (Zhang & Sennrich, 2019), with
       o = residual + sum_j w_j * y_j (+ shared); both o and n are layer outputs.
-  R11 intermediates are not rounded here (fp64 throughout).
+  R11 "W4A16 with BF16 activations": the FFN's activations are BF16 values, so the
+      hidden h (the down projection's input) and the expert output y are rounded to
+      BF16 (nearest, ties to even); every sum and the combine/norm are fp64, and the
+      layer outputs o and n are left unrounded.
 
 Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
 (closed forms, library routines, brute force on tiny inputs, invariants).
@@ -41,8 +44,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "bf16_value", "e2m1_value", "e4m3_value", "unpack_codes", "dequant",
-    "router_logits", "route", "permute", "swiglu_ffn", "expert_outputs",
+    "bf16_value", "bf16_round", "e2m1_value", "e4m3_value", "unpack_codes", "dequant",
+    "router_logits", "route", "permute", "swiglu_hidden", "swiglu_ffn", "expert_outputs",
     "combine_norm", "layer",
 ]
 
@@ -54,6 +57,19 @@ def bf16_value(bits: np.ndarray) -> np.ndarray:
     """BF16 bit patterns (uint16) -> fp64. BF16 is the top half of an IEEE binary32."""
     b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+def bf16_round(v: np.ndarray) -> np.ndarray:
+    """fp64 -> the nearest BF16 value (ties to even), returned as fp64.
+
+    BF16 keeps 8 significant bits: with v = m * 2^e (0.5 <= |m| < 1), v * 2^(8-e) is
+    rounded to an integer (np.rint rounds half to even). Below the normal range the
+    grid stays 2^-133 (the BF16 subnormal step). Finite inputs only.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    e = np.maximum(e, -125)
+    return np.ldexp(np.rint(np.ldexp(v, 8 - e)), e - 8)
 
 
 def e2m1_value(code: np.ndarray) -> np.ndarray:
@@ -100,9 +116,10 @@ def dequant(packed: np.ndarray, scales: np.ndarray, tscale: float) -> np.ndarray
     ``packed`` is [N, K/2], ``scales`` [N, K/16] E4M3 codes, ``tscale`` the FP32
     tensor scale; weight[n, k] = e2m1(code[n, k]) * e4m3(scales[n, k // 16]) * tscale.
     """
+    # decode through the 16 / 256 possible codes (same functions, applied once each)
     codes = unpack_codes(packed)
-    block = np.repeat(e4m3_value(scales), 16, axis=-1)
-    return e2m1_value(codes) * block * float(tscale)
+    block = np.repeat(e4m3_value(np.arange(256))[scales], 16, axis=-1)
+    return e2m1_value(np.arange(16))[codes] * block * float(tscale)
 
 
 # ----------------------------------------------------------------------------
@@ -160,16 +177,25 @@ def permute(idx: np.ndarray, E: int):
 # ----------------------------------------------------------------------------
 # Expert FFN (W4A16 SwiGLU), reading R5
 # ----------------------------------------------------------------------------
-def swiglu_ffn(x: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
-    """y = W2 (silu(Wg x) * (Wu x)) for each row of x (fp64).
+def swiglu_hidden(x: np.ndarray, w13: np.ndarray) -> np.ndarray:
+    """a = silu(Wg x) * (Wu x) for each row of x (fp64), silu(g) = g / (1 + e^-g).
 
-    x [R, H]; w13 [2I, H] (gate rows first, then up rows); w2 [H, I].
+    x [R, H]; w13 [2I, H] (gate rows first, then up rows).
     """
     I = w13.shape[0] // 2
     g = x @ w13[:I].T
     u = x @ w13[I:].T
-    a = g / (1.0 + np.exp(-g)) * u
-    return a @ w2.T
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def swiglu_ffn(x: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """y = W2 (silu(Wg x) * (Wu x)) for each row of x; w2 [H, I].
+
+    The BF16 activations of reading R11: h is rounded to BF16 before the down
+    projection and y is rounded to BF16; the sums are fp64.
+    """
+    h = bf16_round(swiglu_hidden(x, w13))
+    return bf16_round(h @ w2.T)
 
 
 def expert_outputs(x_bits, idx, w13, w2, tokens=None, cache=None) -> np.ndarray:

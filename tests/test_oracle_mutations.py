@@ -71,6 +71,16 @@ def _swiglu_swapped(x, w13, w2):
     return _orig["swiglu_ffn"](x, np.concatenate([w13[I:], w13[:I]]), w2)
 
 
+def _hidden_swapped(x, w13):
+    I = w13.shape[0] // 2
+    return _orig["swiglu_hidden"](x, np.concatenate([w13[I:], w13[:I]]))
+
+
+def _hidden_no_silu(x, w13):
+    I = w13.shape[0] // 2
+    return (x @ w13[:I].T) * (x @ w13[I:].T)
+
+
 def _swiglu_w2_transposed_use(x, w13, w2):
     I = w13.shape[0] // 2
     g = x @ w13[:I].T
@@ -92,7 +102,18 @@ def _combine_shared_dropped(y, w, residual_bits, gamma_bits, eps, shared=None):
     return _orig["combine_norm"](y, w, residual_bits, gamma_bits, eps, None)
 
 
+def _bf16_truncate(v):
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    return np.ldexp(np.trunc(np.ldexp(v, 8 - e)), e - 8)
+
+
+def _ffn_unrounded(x, w13, w2):
+    return oracle.swiglu_hidden(x, w13) @ w2.T
+
+
 MUTANTS = {
+    "bf16_round": [_bf16_truncate],
     "e2m1_value": [_e2m1_bias0],
     "e4m3_value": [_e4m3_bias8],
     "unpack_codes": [_unpack_high_first],
@@ -100,7 +121,8 @@ MUTANTS = {
     "router_logits": [_router_drop_last_term],
     "route": [_route_no_renorm, _route_ties_high],
     "permute": [_permute_unstable],
-    "swiglu_ffn": [_swiglu_swapped, _swiglu_w2_transposed_use],
+    "swiglu_hidden": [_hidden_swapped, _hidden_no_silu],
+    "swiglu_ffn": [_swiglu_swapped, _swiglu_w2_transposed_use, _ffn_unrounded],
     "combine_norm": [_combine_no_residual, _combine_no_gamma, _combine_shared_dropped],
 }
 

@@ -56,6 +56,47 @@ def test_bf16_value_matches_torch():
     assert np.array_equal(oracle.bf16_value(bits), ref)
 
 
+def _rne_bf16_exact(v: float) -> float:
+    """Round to 8 significant bits, ties to even, in exact rationals (normal range)."""
+    if v == 0:
+        return v
+    f = Fraction(v)
+    sign = -1 if f < 0 else 1
+    f = abs(f)
+    e = 0
+    while f >= 2:
+        f /= 2
+        e += 1
+    while f < 1:
+        f *= 2
+        e -= 1
+    q = f * 128
+    n = math.floor(q)
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * float(Fraction(n, 128) * Fraction(2) ** e)
+
+
+def test_bf16_round_exact_rationals_and_ties():
+    rng = np.random.default_rng(12)
+    v = rng.standard_normal(2000) * np.exp2(rng.integers(-30, 30, 2000))
+    # exact ties: a BF16 value plus half its ulp, and the same minus half
+    base = oracle.bf16_value(rng.integers(0x3000, 0x4F00, 200).astype(np.uint16))
+    half = np.exp2(np.floor(np.log2(base)) - 8)
+    v = np.concatenate([v, base + half, base - half, -(base + half), [0.0, -0.0]])
+    got = oracle.bf16_round(v)
+    want = np.array([_rne_bf16_exact(float(a)) for a in v])
+    assert np.array_equal(got, want)
+
+
+def test_bf16_round_matches_torch_on_float32_values():
+    rng = np.random.default_rng(13)
+    v = (rng.standard_normal(100000) * 1e3).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.bf16_round(v.astype(np.float64)), ref)
+
+
 def test_unpack_codes_low_nibble_first():
     rng = np.random.default_rng(2)
     codes = rng.integers(0, 16, (3, 64)).astype(np.uint8)
@@ -177,8 +218,11 @@ def test_permute_empty():
 # ----------------------------------------------------------------------------
 # Expert FFN
 # ----------------------------------------------------------------------------
-def _brute_swiglu(x, w13, w2):
-    """Pure-Python loops, math.exp: independent of numpy's matmul."""
+def _brute_swiglu(x, w13, w2, bf16_acts=True):
+    """Pure-Python loops, math.exp, exact-rational rounding: independent of numpy's
+    matmul and of the oracle's rounding. With bf16_acts the hidden and output
+    activations are rounded to BF16 as W4A16 prescribes."""
+    rnd = _rne_bf16_exact if bf16_acts else (lambda v: v)
     R, H = x.shape
     I = w13.shape[0] // 2
     out = np.zeros((R, w2.shape[0]))
@@ -187,9 +231,9 @@ def _brute_swiglu(x, w13, w2):
         for i in range(I):
             g = math.fsum(float(x[r, h]) * float(w13[i, h]) for h in range(H))
             u = math.fsum(float(x[r, h]) * float(w13[I + i, h]) for h in range(H))
-            a.append(g / (1.0 + math.exp(-g)) * u)
+            a.append(rnd(g / (1.0 + math.exp(-g)) * u))
         for n in range(w2.shape[0]):
-            out[r, n] = math.fsum(float(w2[n, i]) * a[i] for i in range(I))
+            out[r, n] = rnd(math.fsum(float(w2[n, i]) * a[i] for i in range(I)))
     return out
 
 
@@ -201,7 +245,17 @@ def test_swiglu_ffn_brute_force():
                          wl.to_e4m3_codes(np.exp2(rng.uniform(-4, 2, (2 * I, H // 16)))), 1.0)
     w2 = oracle.dequant(rng.integers(0, 256, (H, I // 2)).astype(np.uint8),
                         wl.to_e4m3_codes(np.exp2(rng.uniform(-4, 2, (H, I // 16)))), 1.0)
-    np.testing.assert_allclose(oracle.swiglu_ffn(x, w13, w2), _brute_swiglu(x, w13, w2), rtol=1e-11, atol=1e-9)
+    got = oracle.swiglu_ffn(x, w13, w2)
+    want = _brute_swiglu(x, w13, w2)
+    # BF16 outputs: equal, except where fp64 summation order moves a value across a
+    # rounding boundary (then one BF16 ulp apart)
+    ulp = np.exp2(np.floor(np.log2(np.abs(want))) - 7)
+    assert np.all(np.abs(got - want) <= ulp)
+    assert np.mean(got == want) > 0.98
+    # the hidden activation alone (unrounded): brute force with W2 = identity
+    eye = np.eye(I)
+    np.testing.assert_allclose(oracle.swiglu_hidden(x, w13), _brute_swiglu(x, w13, eye, bf16_acts=False),
+                               rtol=1e-11, atol=1e-9)
 
 
 def test_e1_k1_layer_is_a_dense_swiglu_mlp_via_torch():
@@ -226,7 +280,9 @@ def test_e1_k1_layer_is_a_dense_swiglu_mlp_via_torch():
     W13, W2 = deq(inp.w13), deq(inp.w2)
     I = w.I
     hmid = torch.nn.functional.silu(x @ W13[:I].T) * (x @ W13[I:].T)
-    o = r + hmid @ W2.T
+    # BF16 activations (rounding pinned on its own above)
+    hmid = torch.from_numpy(oracle.bf16_round(hmid.numpy()))
+    o = r + torch.from_numpy(oracle.bf16_round((hmid @ W2.T).numpy()))
     n = torch.nn.functional.rms_norm(o, (w.H,), weight=g, eps=w.eps)
     np.testing.assert_allclose(out["o"], o.numpy(), rtol=1e-12, atol=1e-10)
     np.testing.assert_allclose(out["n"], n.numpy(), rtol=1e-12, atol=1e-10)

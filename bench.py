@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Bench of the W4A16 MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config decode_t8]
+
+A step is one MoE layer call (route -> permute -> expert up -> expert down ->
+combine+RMSNorm) over one batch of synthetic tokens, inputs resident in HBM. The
+default workload is decode with T=8 tokens (H=2048, E=128 experts, top-8, I=768,
+router logits computed from BF16 router weights). Weight copies are rotated so
+the working set is at least 1 GiB, which keeps the 256 MB Infinity Cache from
+serving the weights.
+
+Two timed passes:
+  1. the headline: K fused ``moe4_layer`` calls between two events on the launch
+     stream (value = tokens / s, ms_per_step);
+  2. the roofline: K steps through the separate entry points with events around
+     each launch of the dominant kernel (the expert "up" pass, W13 + SwiGLU), whose
+     algorithmic bytes (touched experts' packed weights + scales, activations in,
+     h out) or flops divided by its mean duration give ``roofline.achieved``.
+The fp64 oracle is timed on the host on a bounded sample (``cpu_baseline``).
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA TFLOP/s as % of peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MALL_DEFEAT_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--config", default="decode_t8")
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def up_kernel_work(inp, idx):
+    """Algorithmic bytes and flops of one expert-up launch for this routing."""
+    w = inp.w
+    distinct = len(set(idx.reshape(-1).tolist()))
+    per_expert = 2 * w.I * w.H // 2 + 2 * w.I * w.H // 16 + 4   # nibbles + E4M3 scales + tscale
+    pairs = inp.T * w.k
+    act_in = inp.T * w.H * 2                                    # x, each token read once
+    h_out = pairs * w.I * 2
+    plan = (w.E + 1) * 4 + pairs * 4
+    nbytes = distinct * per_expert + act_in + h_out + plan
+    flops = 2 * pairs * w.H * (2 * w.I)
+    if w.n_shared:
+        nbytes += per_expert + inp.T * w.I * 2
+        flops += 2 * inp.T * w.H * 2 * w.I
+    return nbytes, flops, distinct
+
+
+def cpu_baseline(inp, budget_s):
+    """Time the oracle as it stands on the host, one thread, on a bounded sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    T = inp.T
+    per_call = T
+    sample_tokens = None
+    if inp.w.T > 64:  # prefill shapes: a seeded sample of tokens
+        sample_tokens = np.sort(np.random.default_rng(7).choice(inp.T, 16, replace=False))
+        per_call = len(sample_tokens)
+    reps, t_used = 0, 0.0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            oracle.layer(inp, tokens=sample_tokens)
+            reps += 1
+            t_used = time.perf_counter() - t0
+            if t_used >= budget_s or reps >= 1000:
+                break
+    what = (f"{reps} oracle layer calls on the same {per_call}-token batch"
+            if sample_tokens is None else f"{reps} oracle calls on 16 sampled tokens of the {T}-token batch")
+    return {"value": reps * per_call / t_used, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{what}; numpy fp64 with BLAS limited to 1 thread; {t_used:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (got --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bit_moe_expert_amd import binding as B
+    from bit_moe_expert_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = wl.workload(args.config)
+    chunks = w.chunks
+    log(f"generating inputs: {w}")
+    t_gen = time.perf_counter()
+    inputs = [wl.make_inputs(w, seed=0, chunk=c) for c in range(chunks)] if chunks > 1 else [wl.make_inputs(w, seed=0)]
+    inp = inputs[0]
+    log(f"inputs ready in {time.perf_counter() - t_gen:.1f} s")
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
+    w13 = B.DeviceW4.from_host(inp.w13)
+    w2 = B.DeviceW4.from_host(inp.w2)
+    s13 = B.DeviceW4.from_host(inp.shared13) if inp.shared13 is not None else None
+    s2 = B.DeviceW4.from_host(inp.shared2) if inp.shared2 is not None else None
+    wr = dev(inp.w_router) if inp.w_router is not None else None
+    wbytes = w13.nbytes + w2.nbytes
+    copies = args.copies or max(1, math.ceil(MALL_DEFEAT_BYTES / wbytes))
+    weights = [(w13, w2)] + [(w13.clone(), w2.clone()) for _ in range(copies - 1)]
+    log(f"weights {wbytes / 1e6:.1f} MB x {copies} copies")
+
+    T = inp.T
+    shape = B.make_shape(T, w.H, w.E, w.k, w.I, w.n_shared, w.eps)
+    per_chunk = []
+    for ci in inputs:
+        per_chunk.append(dict(
+            x=dev(ci.x), residual=dev(ci.residual),
+            logits=dev(ci.logits) if ci.logits is not None else torch.empty((T, w.E), dtype=torch.float32, device="cuda")))
+    gamma = dev(inp.gamma)
+    topk_idx = torch.empty((T, w.k), dtype=torch.int32, device="cuda")
+    topk_w = torch.empty((T, w.k), dtype=torch.float32, device="cuda")
+    res_out = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
+    norm_out = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
+    ws = torch.empty(B.moe4_layer_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+
+    def layer_step(i):
+        c = per_chunk[i % chunks]
+        a13, a2 = weights[(i // chunks) % copies]
+        B.moe4_layer(shape, c["x"], wr, c["logits"], a13, a2, s13, s2, c["residual"], gamma, topk_idx,
+                     topk_w, res_out, norm_out, ws)
+
+    stream = torch.cuda.current_stream()
+    calls_per_step = chunks
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup * calls_per_step):
+        layer_step(i)
+    torch.cuda.synchronize()
+
+    # ---- pass 1: headline ----
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps * calls_per_step):
+        layer_step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    tokens_per_step = T * chunks
+    value = tokens_per_step * args.steps / (ms_total / 1e3)
+    log(f"pass 1: {ms_per_step * 1e3:.2f} us/step, {value:.1f} tokens/s (wall {wall:.3f} s)")
+
+    # ---- pass 2: dominant kernel (expert up) timed with events ----
+    pairs = T * w.k
+    offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
+    perm_src = torch.empty(pairs, dtype=torch.int32, device="cuda")
+    inv = torch.empty(pairs, dtype=torch.int32, device="cuda")
+    pws_n = B.moe4_permute_workspace_bytes(shape)
+    pws = torch.empty(pws_n, dtype=torch.uint8, device="cuda") if pws_n else None
+    h = torch.empty((pairs, w.I), dtype=torch.int16, device="cuda")
+    y = torch.empty((pairs, w.H), dtype=torch.int16, device="cuda")
+    hs = torch.empty((T, w.I), dtype=torch.int16, device="cuda") if w.n_shared else None
+    ys = torch.empty((T, w.H), dtype=torch.int16, device="cuda") if w.n_shared else None
+    k2 = min(args.steps, 400)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(k2 * chunks)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(k2 * chunks)]
+    routing = []
+    for i in range(k2 * chunks):
+        c = per_chunk[i % chunks]
+        a13, a2 = weights[(i // chunks) % copies]
+        B.moe4_route(shape, c["x"] if wr is not None else None, wr, c["logits"], topk_idx, topk_w)
+        B.moe4_permute(shape, topk_idx, offsets, perm_src, inv, pws)
+        starts[i].record(stream)
+        B.moe4_expert_up(shape, c["x"], offsets, perm_src, a13, h)
+        ends[i].record(stream)
+        B.moe4_expert_down(shape, h, offsets, a2, y)
+        if w.n_shared:
+            B.moe4_expert_ffn(shape, c["x"], None, None, s13, s2, hs, ys)
+        B.moe4_combine_norm(shape, y, inv, topk_w, ys, c["residual"], gamma, res_out, norm_out)
+        if i < chunks:
+            torch.cuda.synchronize()
+            routing.append(topk_idx.cpu().numpy())
+    torch.cuda.synchronize()
+    up_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    up_mean_s = float(np.mean(up_ms)) / 1e3
+    nbytes, flops, distinct = 0, 0, []
+    for ci, idx in zip(inputs, routing):
+        b, f, d = up_kernel_work(ci, idx)
+        nbytes += b
+        flops += f
+        distinct.append(d)
+    nbytes /= chunks
+    flops /= chunks
+    log(f"pass 2: expert-up mean {up_mean_s * 1e6:.2f} us over {len(up_ms)} launches; "
+        f"{nbytes / 1e6:.1f} MB, {flops / 1e9:.2f} GFLOP per launch; distinct experts {distinct}")
+
+    hbm_bound = flops / nbytes < 300.0
+    if hbm_bound:
+        achieved = nbytes / up_mean_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = flops / up_mean_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roofline.update({"kernel": "ffn_small_m_kernel<up> (W13 dequant-MFMA + SwiGLU)",
+                     "mean_us": round(up_mean_s * 1e6, 3), "algorithmic_bytes": int(nbytes),
+                     "algorithmic_flops": int(flops)})
+
+    cfg = {"workload": f"{args.config}: T={T}{'x%d chunks' % chunks if chunks > 1 else ''} H={w.H} "
+                       f"E={w.E}{'+%d shared' % w.n_shared if w.n_shared else ''} top-{w.k} I={w.I}, "
+                       f"W4A16 (E2M1 + E4M3/16 + FP32)",
+           "T": T * chunks, "H": w.H, "E": w.E, "k": w.k, "I": w.I, "n_shared": w.n_shared,
+           "weight_copies_rotated": copies, "routing": w.routing}
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": cfg, "roofline": roofline}
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,152 @@
+"""Thin torch binding over the libmoe4 C ABI: argument marshalling only.
+
+Each function has the name of the C entry point it calls and takes torch tensors
+that already live on the GPU (BF16 tensors may be ``torch.bfloat16`` or the raw
+``uint16``/``int16`` bits). Work is enqueued on the current torch stream (or the
+one given); nothing is synchronised or computed here.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import Shape, W4, check
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtypes=None, numel: Optional[int] = None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def make_shape(T: int, H: int, E: int, k: int, I: int, n_shared: int = 0, eps: float = 1e-6) -> Shape:
+    return Shape(T, H, E, k, I, n_shared, eps)
+
+
+@dataclass
+class DeviceW4:
+    """A grouped 4-bit weight tensor resident on the GPU."""
+    packed: torch.Tensor   # uint8 [G, N, K/2]
+    scales: torch.Tensor   # uint8 [G, N, K/16]
+    tscale: torch.Tensor   # float32 [G]
+
+    @classmethod
+    def from_host(cls, w, device="cuda") -> "DeviceW4":
+        return cls(torch.from_numpy(w.packed).to(device),
+                   torch.from_numpy(w.scales).to(device),
+                   torch.from_numpy(w.tscale).to(device))
+
+    def clone(self) -> "DeviceW4":
+        return DeviceW4(self.packed.clone(), self.scales.clone(), self.tscale.clone())
+
+    def desc(self) -> W4:
+        return W4(_ptr(self.packed, "packed", (torch.uint8,)),
+                  _ptr(self.scales, "scales", (torch.uint8,)),
+                  _ptr(self.tscale, "tscale", (torch.float32,)))
+
+    @property
+    def nbytes(self) -> int:
+        return self.packed.numel() + self.scales.numel() + 4 * self.tscale.numel()
+
+
+def moe4_permute_workspace_bytes(shape: Shape) -> int:
+    return int(_lib.load().moe4_permute_workspace_bytes(shape))
+
+
+def moe4_layer_workspace_bytes(shape: Shape) -> int:
+    return int(_lib.load().moe4_layer_workspace_bytes(shape))
+
+
+def moe4_route(shape: Shape, x, w_router, logits, topk_idx, topk_w, stream=None) -> None:
+    T, E, k, H = shape.T, shape.E, shape.k, shape.H
+    check(_lib.load().moe4_route(
+        shape, _ptr(x, "x", _BF16_LIKE, T * H), _ptr(w_router, "w_router", _BF16_LIKE, E * H),
+        _ptr(logits, "logits", (torch.float32,), T * E),
+        _ptr(topk_idx, "topk_idx", (torch.int32,), T * k),
+        _ptr(topk_w, "topk_w", (torch.float32,), T * k), _stream(stream)))
+
+
+def moe4_permute(shape: Shape, topk_idx, offsets, perm_src, inv, ws=None, stream=None) -> None:
+    n = shape.T * shape.k
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    check(_lib.load().moe4_permute(
+        shape, _ptr(topk_idx, "topk_idx", (torch.int32,), n),
+        _ptr(offsets, "offsets", (torch.int32,), shape.E + 1),
+        _ptr(perm_src, "perm_src", (torch.int32,), n), _ptr(inv, "inv", (torch.int32,), n),
+        _ptr(ws, "ws"), ws_bytes, _stream(stream)))
+
+
+def moe4_expert_ffn(shape: Shape, x, offsets, perm_src, w13: DeviceW4, w2: DeviceW4, h, y,
+                    stream=None) -> None:
+    rows = shape.T * shape.k if offsets is not None else shape.T
+    d13, d2 = w13.desc(), w2.desc()
+    check(_lib.load().moe4_expert_ffn(
+        shape, _ptr(x, "x", _BF16_LIKE, shape.T * shape.H),
+        _ptr(offsets, "offsets", (torch.int32,)), _ptr(perm_src, "perm_src", (torch.int32,)),
+        d13, d2, _ptr(h, "h", _BF16_LIKE, rows * shape.I), _ptr(y, "y", _BF16_LIKE, rows * shape.H),
+        _stream(stream)))
+
+
+def moe4_expert_up(shape: Shape, x, offsets, perm_src, w13: DeviceW4, h, stream=None) -> None:
+    rows = shape.T * shape.k if offsets is not None else shape.T
+    d13 = w13.desc()
+    check(_lib.load().moe4_expert_up(
+        shape, _ptr(x, "x", _BF16_LIKE, shape.T * shape.H),
+        _ptr(offsets, "offsets", (torch.int32,)), _ptr(perm_src, "perm_src", (torch.int32,)),
+        d13, _ptr(h, "h", _BF16_LIKE, rows * shape.I), _stream(stream)))
+
+
+def moe4_expert_down(shape: Shape, h, offsets, w2: DeviceW4, y, stream=None) -> None:
+    rows = shape.T * shape.k if offsets is not None else shape.T
+    d2 = w2.desc()
+    check(_lib.load().moe4_expert_down(
+        shape, _ptr(h, "h", _BF16_LIKE, rows * shape.I), _ptr(offsets, "offsets", (torch.int32,)),
+        d2, _ptr(y, "y", _BF16_LIKE, rows * shape.H), _stream(stream)))
+
+
+def moe4_combine_norm(shape: Shape, y, inv, topk_w, shared_y, residual, gamma, residual_out,
+                      normed_out, stream=None) -> None:
+    T, H, k = shape.T, shape.H, shape.k
+    check(_lib.load().moe4_combine_norm(
+        shape, _ptr(y, "y", _BF16_LIKE, T * k * H), _ptr(inv, "inv", (torch.int32,), T * k),
+        _ptr(topk_w, "topk_w", (torch.float32,), T * k),
+        _ptr(shared_y, "shared_y", _BF16_LIKE, T * H), _ptr(residual, "residual", _BF16_LIKE, T * H),
+        _ptr(gamma, "gamma", _BF16_LIKE, H), _ptr(residual_out, "residual_out", _BF16_LIKE, T * H),
+        _ptr(normed_out, "normed_out", _BF16_LIKE, T * H), _stream(stream)))
+
+
+def moe4_layer(shape: Shape, x, w_router, logits, w13: DeviceW4, w2: DeviceW4,
+               shared13: Optional[DeviceW4], shared2: Optional[DeviceW4], residual, gamma,
+               topk_idx, topk_w, residual_out, normed_out, ws, stream=None) -> None:
+    T, H, E, k = shape.T, shape.H, shape.E, shape.k
+    d13, d2 = w13.desc(), w2.desc()
+    s13 = shared13.desc() if shared13 is not None else None
+    s2 = shared2.desc() if shared2 is not None else None
+    check(_lib.load().moe4_layer(
+        shape, _ptr(x, "x", _BF16_LIKE, T * H), _ptr(w_router, "w_router", _BF16_LIKE, E * H),
+        _ptr(logits, "logits", (torch.float32,), T * E), d13, d2, s13, s2,
+        _ptr(residual, "residual", _BF16_LIKE, T * H), _ptr(gamma, "gamma", _BF16_LIKE, H),
+        _ptr(topk_idx, "topk_idx", (torch.int32,), T * k),
+        _ptr(topk_w, "topk_w", (torch.float32,), T * k),
+        _ptr(residual_out, "residual_out", _BF16_LIKE, T * H),
+        _ptr(normed_out, "normed_out", _BF16_LIKE, T * H),
+        _ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))

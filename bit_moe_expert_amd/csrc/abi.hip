@@ -1,0 +1,323 @@
+// libmoe4 C ABI: argument checks, workspace layout and launch order.
+// Everything is checked before the first launch, so an invalid call enqueues nothing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe4.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe4_status fail(moe4_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe4_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define NEED(p, name)                                                                  \
+  do {                                                                                 \
+    if ((p) == nullptr) return fail(MOE4_ERR_INVALID_ARG, "%s is NULL", name);         \
+    if (!aligned16(p)) return fail(MOE4_ERR_INVALID_ARG, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+moe4_status check_shape(const moe4_shape* s) {
+  if (s == nullptr) return fail(MOE4_ERR_INVALID_ARG, "shape is NULL");
+  if (s->T < 0 || s->H <= 0 || s->E <= 0 || s->k <= 0 || s->I <= 0)
+    return fail(MOE4_ERR_INVALID_ARG, "shape has a negative or zero size (T=%d H=%d E=%d k=%d I=%d)",
+                s->T, s->H, s->E, s->k, s->I);
+  if (!(s->eps > 0.0f)) return fail(MOE4_ERR_INVALID_ARG, "eps must be > 0");
+  if (s->n_shared != 0 && s->n_shared != 1)
+    return fail(MOE4_ERR_UNSUPPORTED, "n_shared must be 0 or 1 (got %d)", s->n_shared);
+  if (s->E > 256) return fail(MOE4_ERR_UNSUPPORTED, "E=%d > 256", s->E);
+  if (s->k > 16 || s->k > s->E) return fail(MOE4_ERR_UNSUPPORTED, "k=%d must be <= min(E, 16)", s->k);
+  if (s->H % 128 || s->H < 128 || s->H > 16384)
+    return fail(MOE4_ERR_UNSUPPORTED, "H=%d must be a multiple of 128 in [128, 16384]", s->H);
+  if (s->I % 128 || s->I < 128 || s->I > 16384)
+    return fail(MOE4_ERR_UNSUPPORTED, "I=%d must be a multiple of 128 in [128, 16384]", s->I);
+  if (s->T > (1 << 20)) return fail(MOE4_ERR_UNSUPPORTED, "T=%d > 2^20", s->T);
+  if ((long long)s->T * s->k >= (1LL << 31)) return fail(MOE4_ERR_UNSUPPORTED, "T*k >= 2^31");
+  return MOE4_OK;
+}
+
+moe4_status check_w4(const moe4_w4* w, const char* name) {
+  if (w == nullptr) return fail(MOE4_ERR_INVALID_ARG, "%s descriptor is NULL", name);
+  char buf[64];
+  snprintf(buf, sizeof(buf), "%s.packed", name);
+  NEED(w->packed, buf);
+  snprintf(buf, sizeof(buf), "%s.scales", name);
+  if (w->scales == nullptr) return fail(MOE4_ERR_INVALID_ARG, "%s is NULL", buf);
+  // scale rows are K/16 bytes: 8-byte multiples for K % 128 == 0; need 2-byte alignment
+  if (reinterpret_cast<uintptr_t>(w->scales) & 1u)
+    return fail(MOE4_ERR_INVALID_ARG, "%s is not 2-byte aligned", buf);
+  snprintf(buf, sizeof(buf), "%s.tscale", name);
+  if (w->tscale == nullptr) return fail(MOE4_ERR_INVALID_ARG, "%s is NULL", buf);
+  if (reinterpret_cast<uintptr_t>(w->tscale) & 3u)
+    return fail(MOE4_ERR_INVALID_ARG, "%s is not 4-byte aligned", buf);
+  return MOE4_OK;
+}
+
+moe4::W4View view(const moe4_w4* w) { return moe4::W4View{w->packed, w->scales, w->tscale}; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct LayerWs {
+  size_t offsets, perm_src, inv, perm_ws, h, y, total;
+};
+
+LayerWs layer_ws_layout(const moe4_shape* s) {
+  LayerWs l{};
+  const size_t pairs = (size_t)s->T * s->k;
+  const size_t rows = pairs + (size_t)s->T * s->n_shared;
+  size_t o = 0;
+  l.offsets = o; o += align256((size_t)(s->E + 1) * 4);
+  l.perm_src = o; o += align256(pairs * 4);
+  l.inv = o;      o += align256(pairs * 4);
+  l.perm_ws = o;  o += align256(moe4::permute_workspace_bytes((long long)pairs, s->E));
+  l.h = o;        o += align256(rows * s->I * 2);
+  l.y = o;        o += align256(rows * s->H * 2);
+  l.total = o;
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe4_abi_version(void) { return MOE4_ABI_VERSION; }
+
+const char* moe4_last_error(void) { return g_err; }
+
+size_t moe4_permute_workspace_bytes(const moe4_shape* shape) {
+  if (check_shape(shape) != MOE4_OK) return 0;
+  return moe4::permute_workspace_bytes((long long)shape->T * shape->k, shape->E);
+}
+
+size_t moe4_layer_workspace_bytes(const moe4_shape* shape) {
+  if (check_shape(shape) != MOE4_OK) return 0;
+  return layer_ws_layout(shape).total;
+}
+
+moe4_status moe4_route(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                       float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  g_err[0] = 0;
+  moe4_status st = check_shape(shape);
+  if (st) return st;
+  if (shape->T == 0) return MOE4_OK;  // nothing to read or write
+  if ((x == nullptr) != (w_router == nullptr))
+    return fail(MOE4_ERR_INVALID_ARG, "x and w_router must both be set or both be NULL");
+  if (x) {
+    NEED(x, "x");
+    NEED(w_router, "w_router");
+  }
+  NEED(logits, "logits");
+  NEED(topk_idx, "topk_idx");
+  NEED(topk_w, "topk_w");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (x) {
+    e = moe4::launch_router_logits(x, w_router, logits, shape->T, shape->H, shape->E, s);
+    if (e != hipSuccess) return hip_fail(e, "router_logits launch");
+  }
+  e = moe4::launch_topk_softmax(logits, topk_idx, topk_w, shape->T, shape->E, shape->k, s);
+  if (e != hipSuccess) return hip_fail(e, "topk_softmax launch");
+  return MOE4_OK;
+}
+
+moe4_status moe4_permute(const moe4_shape* shape, const int32_t* topk_idx, int32_t* offsets,
+                         int32_t* perm_src, int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe4_status st = check_shape(shape);
+  if (st) return st;
+  if (shape->T == 0) return MOE4_OK;  // nothing to read or write
+  NEED(topk_idx, "topk_idx");
+  NEED(offsets, "offsets");
+  NEED(perm_src, "perm_src");
+  NEED(inv, "inv");
+  const long long n = (long long)shape->T * shape->k;
+  const size_t need = moe4::permute_workspace_bytes(n, shape->E);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need)
+      return fail(MOE4_ERR_WORKSPACE, "permute needs %zu workspace bytes, got %zu%s", need, ws_bytes,
+                  ws ? "" : " (NULL)");
+    if (!aligned16(ws)) return fail(MOE4_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  }
+  hipError_t e = moe4::launch_permute(topk_idx, n, shape->E, offsets, perm_src, inv, ws,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "permute launch");
+  return MOE4_OK;
+}
+
+moe4_status moe4_expert_ffn(const moe4_shape* shape, const uint16_t* x, const int32_t* offsets,
+                            const int32_t* perm_src, const moe4_w4* w13, const moe4_w4* w2,
+                            uint16_t* h, uint16_t* y, void* stream) {
+  g_err[0] = 0;
+  moe4_status st = check_shape(shape);
+  if (st) return st;
+  if (shape->T == 0) return MOE4_OK;  // nothing to read or write
+  if ((offsets == nullptr) != (perm_src == nullptr))
+    return fail(MOE4_ERR_INVALID_ARG, "offsets and perm_src must both be set or both be NULL");
+  NEED(x, "x");
+  if (offsets) {
+    NEED(offsets, "offsets");
+    NEED(perm_src, "perm_src");
+  }
+  if ((st = check_w4(w13, "w13"))) return st;
+  if ((st = check_w4(w2, "w2"))) return st;
+  NEED(h, "h");
+  NEED(y, "y");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool dense = offsets == nullptr;
+  const int G = dense ? 1 : shape->E;
+  hipError_t e = moe4::launch_ffn_up(x, offsets, perm_src, shape->k, shape->T, G, shape->H, shape->I,
+                                     view(w13), h, s);
+  if (e != hipSuccess) return hip_fail(e, "ffn up launch");
+  e = moe4::launch_ffn_down(h, offsets, shape->T, G, shape->H, shape->I, view(w2), y, s);
+  if (e != hipSuccess) return hip_fail(e, "ffn down launch");
+  return MOE4_OK;
+}
+
+moe4_status moe4_expert_up(const moe4_shape* shape, const uint16_t* x, const int32_t* offsets,
+                           const int32_t* perm_src, const moe4_w4* w13, uint16_t* h, void* stream) {
+  g_err[0] = 0;
+  moe4_status st = check_shape(shape);
+  if (st) return st;
+  if (shape->T == 0) return MOE4_OK;  // nothing to read or write
+  if ((offsets == nullptr) != (perm_src == nullptr))
+    return fail(MOE4_ERR_INVALID_ARG, "offsets and perm_src must both be set or both be NULL");
+  NEED(x, "x");
+  if (offsets) {
+    NEED(offsets, "offsets");
+    NEED(perm_src, "perm_src");
+  }
+  if ((st = check_w4(w13, "w13"))) return st;
+  NEED(h, "h");
+  const int G = offsets ? shape->E : 1;
+  hipError_t e = moe4::launch_ffn_up(x, offsets, perm_src, shape->k, shape->T, G, shape->H, shape->I,
+                                     view(w13), h, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ffn up launch");
+  return MOE4_OK;
+}
+
+moe4_status moe4_expert_down(const moe4_shape* shape, const uint16_t* h, const int32_t* offsets,
+                             const moe4_w4* w2, uint16_t* y, void* stream) {
+  g_err[0] = 0;
+  moe4_status st = check_shape(shape);
+  if (st) return st;
+  if (shape->T == 0) return MOE4_OK;  // nothing to read or write
+  NEED(h, "h");
+  if (offsets) NEED(offsets, "offsets");
+  if ((st = check_w4(w2, "w2"))) return st;
+  NEED(y, "y");
+  const int G = offsets ? shape->E : 1;
+  hipError_t e = moe4::launch_ffn_down(h, offsets, shape->T, G, shape->H, shape->I, view(w2), y,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ffn down launch");
+  return MOE4_OK;
+}
+
+moe4_status moe4_combine_norm(const moe4_shape* shape, const uint16_t* y, const int32_t* inv,
+                              const float* topk_w, const uint16_t* shared_y,
+                              const uint16_t* residual, const uint16_t* gamma,
+                              uint16_t* residual_out, uint16_t* normed_out, void* stream) {
+  g_err[0] = 0;
+  moe4_status st = check_shape(shape);
+  if (st) return st;
+  if (shape->T == 0) return MOE4_OK;  // nothing to read or write
+  NEED(y, "y");
+  NEED(inv, "inv");
+  NEED(topk_w, "topk_w");
+  if (shared_y) NEED(shared_y, "shared_y");
+  NEED(residual, "residual");
+  NEED(gamma, "gamma");
+  NEED(residual_out, "residual_out");
+  NEED(normed_out, "normed_out");
+  hipError_t e = moe4::launch_combine_norm(y, inv, topk_w, shared_y, residual, gamma, residual_out,
+                                           normed_out, shape->T, shape->H, shape->k, shape->eps,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "combine_norm launch");
+  return MOE4_OK;
+}
+
+moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                       float* logits, const moe4_w4* w13, const moe4_w4* w2,
+                       const moe4_w4* shared13, const moe4_w4* shared2,
+                       const uint16_t* residual, const uint16_t* gamma, int32_t* topk_idx,
+                       float* topk_w, uint16_t* residual_out, uint16_t* normed_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe4_status st = check_shape(shape);
+  if (st) return st;
+  if (shape->T == 0) return MOE4_OK;  // nothing to read or write
+  NEED(x, "x");
+  if (w_router) NEED(w_router, "w_router");
+  NEED(logits, "logits");
+  if ((st = check_w4(w13, "w13"))) return st;
+  if ((st = check_w4(w2, "w2"))) return st;
+  if (shape->n_shared) {
+    if ((st = check_w4(shared13, "shared13"))) return st;
+    if ((st = check_w4(shared2, "shared2"))) return st;
+  }
+  NEED(residual, "residual");
+  NEED(gamma, "gamma");
+  NEED(topk_idx, "topk_idx");
+  NEED(topk_w, "topk_w");
+  NEED(residual_out, "residual_out");
+  NEED(normed_out, "normed_out");
+  const LayerWs L = layer_ws_layout(shape);
+  if (ws == nullptr || ws_bytes < L.total)
+    return fail(MOE4_ERR_WORKSPACE, "layer needs %zu workspace bytes, got %zu%s", L.total, ws_bytes,
+                ws ? "" : " (NULL)");
+  if (!aligned16(ws)) return fail(MOE4_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+
+  char* base = static_cast<char*>(ws);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* perm_src = reinterpret_cast<int32_t*>(base + L.perm_src);
+  int32_t* inv = reinterpret_cast<int32_t*>(base + L.inv);
+  void* perm_ws = base + L.perm_ws;
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + L.h);
+  uint16_t* y = reinterpret_cast<uint16_t*>(base + L.y);
+  const size_t pairs = (size_t)shape->T * shape->k;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = shape->T, H = shape->H, E = shape->E, k = shape->k, I = shape->I;
+
+  hipError_t e;
+  if (w_router) {
+    e = moe4::launch_router_logits(x, w_router, logits, T, H, E, s);
+    if (e != hipSuccess) return hip_fail(e, "router_logits launch");
+  }
+  e = moe4::launch_topk_softmax(logits, topk_idx, topk_w, T, E, k, s);
+  if (e != hipSuccess) return hip_fail(e, "topk_softmax launch");
+  e = moe4::launch_permute(topk_idx, (long long)pairs, E, offsets, perm_src, inv, perm_ws, s);
+  if (e != hipSuccess) return hip_fail(e, "permute launch");
+  e = moe4::launch_ffn_up(x, offsets, perm_src, k, T, E, H, I, view(w13), h, s);
+  if (e != hipSuccess) return hip_fail(e, "ffn up launch");
+  e = moe4::launch_ffn_down(h, offsets, T, E, H, I, view(w2), y, s);
+  if (e != hipSuccess) return hip_fail(e, "ffn down launch");
+  const uint16_t* shared_y = nullptr;
+  if (shape->n_shared) {
+    uint16_t* hs = h + pairs * I;
+    uint16_t* ys = y + pairs * H;
+    e = moe4::launch_ffn_up(x, nullptr, nullptr, k, T, 1, H, I, view(shared13), hs, s);
+    if (e != hipSuccess) return hip_fail(e, "shared ffn up launch");
+    e = moe4::launch_ffn_down(hs, nullptr, T, 1, H, I, view(shared2), ys, s);
+    if (e != hipSuccess) return hip_fail(e, "shared ffn down launch");
+    shared_y = ys;
+  }
+  e = moe4::launch_combine_norm(y, inv, topk_w, shared_y, residual, gamma, residual_out, normed_out, T,
+                                H, k, shape->eps, s);
+  if (e != hipSuccess) return hip_fail(e, "combine_norm launch");
+  return MOE4_OK;
+}
+
+}  // extern "C"

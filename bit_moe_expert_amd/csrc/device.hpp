@@ -1,0 +1,90 @@
+// Device helpers shared by the libmoe4 kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe4 {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// BF16 <-> FP32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Two FP32 -> packed BF16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float a) { return (uint16_t)(pack_bf16x2(a, 0.f) & 0xffffu); }
+
+// ---------------------------------------------------------------------------
+// 4-bit weights
+// ---------------------------------------------------------------------------
+// E4M3 (OCP) block-scale code in byte `sel` of v -> FP32 (v_cvt_f32_fp8, OCP on gfx950).
+template <int sel>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t v) { return __builtin_amdgcn_cvt_f32_fp8((int)v, sel); }
+
+// Byte `sel` of `codes` (two E2M1 codes, low nibble first) -> two FP32 values.
+// The hardware conversion applies only the exponent of its scale operand, so it is
+// called with 1.0 and the E4M3 block scale is multiplied in afterwards; the product
+// of a 2-significant-bit code and a 4-significant-bit scale is exact in BF16.
+template <int sel>
+__device__ __forceinline__ f32x2 e2m1x2_to_f32(uint32_t codes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, sel);
+}
+
+// Eight codes (one dword, element 0 in the lowest nibble) times one block scale ->
+// eight BF16 weights as 4 dwords, element order preserved (exact).
+__device__ __forceinline__ u32x4 dequant8(uint32_t codes, float s) {
+  f32x2 a = e2m1x2_to_f32<0>(codes);
+  f32x2 b = e2m1x2_to_f32<1>(codes);
+  f32x2 c = e2m1x2_to_f32<2>(codes);
+  f32x2 d = e2m1x2_to_f32<3>(codes);
+  u32x4 r;
+  r[0] = pack_bf16x2(a[0] * s, a[1] * s);
+  r[1] = pack_bf16x2(b[0] * s, b[1] * s);
+  r[2] = pack_bf16x2(c[0] * s, c[1] * s);
+  r[3] = pack_bf16x2(d[0] * s, d[1] * s);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers (operand layouts checked on gfx950):
+//  16x16x32 bf16: lane l supplies A[l%16][kslot(l/16, 0..7)], B[kslot(l/16, 0..7)][l%16];
+//                 D[4*(l/16)+r][l%16] = acc[r].
+//  32x32x16 bf16: lane l supplies A[l%32][kslot(l/32, 0..7)], B[kslot(l/32, 0..7)][l%32];
+//                 D[8*(r/4)+4*(l/32)+r%4][l%32] = acc[r].
+// A and B only have to agree on which K each (lane group, slot) stands for.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Misc
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
+
+}  // namespace moe4

@@ -1,0 +1,43 @@
+// Host-side launchers of the libmoe4 kernels (one per kernel family). Each enqueues
+// on `stream` and returns the launch status; argument checks happen in abi.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe4 {
+
+// Router GEMV: logits[t][e] = sum_h x[t][h] * wr[e][h] (BF16 in, FP32 accumulate).
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H,
+                                int E, hipStream_t s);
+
+// Top-k selection + renormalised softmax over the selected logits.
+hipError_t launch_topk_softmax(const float* logits, int32_t* idx, float* w, int T, int E, int k,
+                               hipStream_t s);
+
+// Stable counting sort of flat pair indices by expert.
+size_t permute_workspace_bytes(long long n, int E);
+hipError_t launch_permute(const int32_t* idx, long long n, int E, int32_t* offsets, int32_t* perm_src,
+                          int32_t* inv, void* ws, hipStream_t s);
+
+// Grouped W4A16 FFN halves.
+struct W4View {
+  const uint8_t* packed;
+  const uint8_t* scales;
+  const float* tscale;
+};
+// h[r] = silu(gate . x[tok(r)]) * (up . x[tok(r)]); offsets/perm_src NULL = dense (G=1, R=T).
+hipError_t launch_ffn_up(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
+                         int T, int G, int H, int I, W4View w13, uint16_t* h, hipStream_t s);
+// y[r] = W2 . h[r]
+hipError_t launch_ffn_down(const uint16_t* h, const int32_t* offsets, int T, int G, int H, int I,
+                           W4View w2, uint16_t* y, hipStream_t s);
+
+// o = residual + sum_j w_j * y[inv[t*k+j]] (+ shared); n = rmsnorm(o) * gamma.
+hipError_t launch_combine_norm(const uint16_t* y, const int32_t* inv, const float* w,
+                               const uint16_t* shared_y, const uint16_t* residual,
+                               const uint16_t* gamma, uint16_t* res_out, uint16_t* norm_out, int T,
+                               int H, int k, float eps, hipStream_t s);
+
+}  // namespace moe4

@@ -1,0 +1,186 @@
+/*
+ * libmoe4 — the quantized (W4A16) mixture-of-experts layer on one MI355X (gfx950).
+ *
+ * The layer is the one the TensorFold issue "GB10: Nemotron decode is 1.4 % (code) /
+ * 3.0 % (prose) slower on 1.0.3 than on 1.0.2" (#627) lays out in its Oct 14 comment
+ * on where a decode step's time goes: router -> topk -> plan -> routed experts, a
+ * shared expert beside them, then add_moe_norm (the weighted MoE sum added to the
+ * residual, then normalised). Weights are NVFP4 read as they are stored and computed
+ * against BF16 activations, i.e. W4A16 (bear-blog article on TensorFold 1.0.12 /
+ * PR804, section "NVFP4 is neither uniform 4-bit nor all-FP4 compute").
+ *
+ * Storage formats (all row-major and contiguous):
+ *   BF16       uint16_t bit patterns.
+ *   weights    4-bit E2M1 codes (1 sign, 2 exponent bits with bias 1, 1 mantissa bit),
+ *              two per byte along K: element 2j in the low nibble, 2j+1 in the high one.
+ *   scales     one OCP FP8 E4M3FN code (bias 7, max 448, 0x7F/0xFF NaN) per 16
+ *              consecutive weights along K.
+ *   tscale     one FP32 tensor scale per expert matrix.
+ *   weight[n][k] = e2m1(code[n][k]) * e4m3(scale[n][k/16]) * tscale.
+ *   W13 (per expert): N = 2I rows, K = H; rows 0..I-1 are the gate, I..2I-1 the up
+ *   projection.  W2 (per expert): N = H rows, K = I.  The shared expert uses the same
+ *   layouts with one expert.
+ *
+ * The expert FFN is SwiGLU: h = silu(gate . x) * (up . x), y = W2 . h.
+ * Routing: softmax over the E logits, the k largest selected (ties -> lower expert
+ * index, output in descending order), their probabilities renormalised to sum to 1.
+ * Combine: o = residual + sum_j w_j * y_j (+ shared expert output); the normalised
+ * output is n = o / sqrt(mean(o^2) + eps) * gamma (RMSNorm).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are caller-owned DEVICE memory, 16-byte aligned, unless a
+ *     comment says otherwise; `shape` and the moe4_w4 descriptors are HOST structs.
+ *   - The library never allocates, frees or synchronises. Work is enqueued on
+ *     `stream` (a hipStream_t passed as void*; NULL = the null stream) and runs
+ *     asynchronously. Calls enqueue no host-device copies, so they can be captured
+ *     into a HIP graph.
+ *   - A returned status covers the synchronous argument checks and launch errors.
+ *     Faults during execution surface at the caller's next synchronisation.
+ *     On any error nothing has been enqueued, except for MOE4_ERR_HIP, where earlier
+ *     launches of the same call may already be queued.
+ *   - Intermediate precisions: router logits FP32; routing weights FP32; h and y
+ *     BF16 (round to nearest even); all sums FP32 in a fixed order, so repeated calls
+ *     on the same inputs give identical bytes.
+ *   - T == 0 is a valid no-op: after the shape check the call returns MOE4_OK without
+ *     looking at any tensor pointer.
+ *   - Envelope: T >= 0, 1 <= k <= min(E, 16), 1 <= E <= 256, H % 128 == 0,
+ *     I % 128 == 0, 128 <= H <= 16384, 128 <= I <= 16384, n_shared in {0, 1},
+ *     T*k < 2^31. Outside it: MOE4_ERR_UNSUPPORTED.
+ *   - Thread safety: calls are reentrant; the only global state is a thread-local
+ *     error string.
+ */
+#ifndef MOE4_H
+#define MOE4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE4_ABI_VERSION 1
+
+typedef enum {
+  MOE4_OK = 0,
+  MOE4_ERR_INVALID_ARG = 1, /* null or misaligned pointer, negative size, bad descriptor */
+  MOE4_ERR_UNSUPPORTED = 2, /* a shape outside the envelope above */
+  MOE4_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  MOE4_ERR_HIP = 4          /* a HIP runtime error; see moe4_last_error() */
+} moe4_status;
+
+/* Layer shape (host struct). */
+typedef struct {
+  int32_t T;        /* tokens in this call */
+  int32_t H;        /* hidden size */
+  int32_t E;        /* routed experts */
+  int32_t k;        /* experts per token */
+  int32_t I;        /* expert FFN intermediate size */
+  int32_t n_shared; /* always-on shared experts: 0 or 1 */
+  float eps;        /* RMSNorm epsilon (> 0) */
+} moe4_shape;
+
+/* One grouped 4-bit weight tensor over G experts (host struct of device pointers).
+ * packed [G][N][K/2], scales [G][N][K/16], tscale [G]. */
+typedef struct {
+  const uint8_t* packed;
+  const uint8_t* scales;
+  const float* tscale;
+} moe4_w4;
+
+/* Version of this header the library was built from (MOE4_ABI_VERSION). */
+int moe4_abi_version(void);
+
+/* Text of the last error on the calling thread ("" if none). Never NULL; owned by the
+ * library and valid until the next call on the same thread. */
+const char* moe4_last_error(void);
+
+/* Bytes of workspace moe4_permute needs for `shape` (host, pure; 0 on a bad shape). */
+size_t moe4_permute_workspace_bytes(const moe4_shape* shape);
+
+/* Bytes of workspace moe4_layer needs for `shape` (host, pure; 0 on a bad shape). */
+size_t moe4_layer_workspace_bytes(const moe4_shape* shape);
+
+/* Router and top-k (#627, Oct 14 comment: "router -> topk"; the BobClawblaw comment
+ * of the same day on keeping the router's wide block grid).
+ *   x         BF16 [T][H] activations, or NULL.
+ *   w_router  BF16 [E][H] router weights, or NULL (both NULL or both set).
+ *   logits    FP32 [T][E]: written (logits[t][e] = sum_h x[t][h] * w_router[e][h],
+ *             FP32 accumulation) when x is set; read as the given logits otherwise.
+ *   topk_idx  int32 [T][k] out: selected experts, descending logit, ties -> lower index.
+ *   topk_w    FP32 [T][k] out: renormalised softmax weights of the selected experts.
+ * NaN logits give unspecified (but in-range) indices. */
+moe4_status moe4_route(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                       float* logits, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* The plan (#627, Oct 14 comment: "plan" between topk and the routed experts): a stable
+ * counting sort of the T*k (token, slot) pairs by expert. Flat pair f = t*k + j.
+ *   topk_idx  int32 [T][k] in, values in [0, E) (others are undefined behaviour).
+ *   offsets   int32 [E+1] out: offsets[e] = number of pairs routed to experts < e.
+ *   perm_src  int32 [T*k] out: rows offsets[e]..offsets[e+1]-1 hold expert e's flat
+ *             pair indices f in ascending order.
+ *   inv       int32 [T*k] out: inv[f] = the row of pair f (perm_src[inv[f]] == f).
+ *   ws        device workspace of at least moe4_permute_workspace_bytes(shape). */
+moe4_status moe4_permute(const moe4_shape* shape, const int32_t* topk_idx, int32_t* offsets,
+                         int32_t* perm_src, int32_t* inv, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Routed experts "up" and "down" (#627, BobClawblaw comment of Oct 14: the expert up
+ * and down kernels are 63 % of decode GPU time), as a grouped W4A16 SwiGLU FFN.
+ *   x         BF16 [T][H] activations.
+ *   offsets, perm_src  the plan from moe4_permute: row r of expert e (offsets[e] <= r <
+ *             offsets[e+1]) takes token perm_src[r] / k. Both NULL selects dense mode:
+ *             one group of T rows, row r = token r, through expert 0 of w13/w2 (the
+ *             shared expert).
+ *   w13, w2   weight descriptors over E experts (dense mode: over 1 expert).
+ *   h         BF16 [R][I] out (R = T*k, dense mode R = T): silu(gate) * up per row.
+ *   y         BF16 [R][H] out: W2 . h per row, in plan order. */
+moe4_status moe4_expert_ffn(const moe4_shape* shape, const uint16_t* x, const int32_t* offsets,
+                            const int32_t* perm_src, const moe4_w4* w13, const moe4_w4* w2,
+                            uint16_t* h, uint16_t* y, void* stream);
+
+/* The two halves of moe4_expert_ffn, for callers that schedule them apart (and for
+ * timing the dominant one alone). Arguments as for moe4_expert_ffn:
+ *   moe4_expert_up:   h [R][I] = silu(gate . x[token(r)]) * (up . x[token(r)]).
+ *   moe4_expert_down: y [R][H] = W2 . h[r]; offsets NULL selects dense mode (R = T). */
+moe4_status moe4_expert_up(const moe4_shape* shape, const uint16_t* x, const int32_t* offsets,
+                           const int32_t* perm_src, const moe4_w4* w13, uint16_t* h, void* stream);
+moe4_status moe4_expert_down(const moe4_shape* shape, const uint16_t* h, const int32_t* offsets,
+                             const moe4_w4* w2, uint16_t* y, void* stream);
+
+/* add_moe_norm (#627, table "Median time per launch" and the Oct 14 comment).
+ *   y         BF16 [T*k][H] expert outputs in plan order.
+ *   inv       int32 [T*k] from moe4_permute.
+ *   topk_w    FP32 [T][k] routing weights.
+ *   shared_y  BF16 [T][H] shared-expert output, or NULL.
+ *   residual  BF16 [T][H]; gamma BF16 [H].
+ *   residual_out BF16 [T][H] out: o = residual + sum_j topk_w[t][j] * y[inv[t*k+j]]
+ *             (+ shared_y[t]), summed in FP32 in the order j = 0..k-1; may alias residual.
+ *   normed_out BF16 [T][H] out: o / sqrt(mean(o^2) + eps) * gamma from the FP32 o. */
+moe4_status moe4_combine_norm(const moe4_shape* shape, const uint16_t* y, const int32_t* inv,
+                              const float* topk_w, const uint16_t* shared_y,
+                              const uint16_t* residual, const uint16_t* gamma,
+                              uint16_t* residual_out, uint16_t* normed_out, void* stream);
+
+/* The whole layer: route -> permute -> routed expert FFN (+ shared expert FFN when
+ * shape->n_shared == 1) -> combine_norm, enqueued on `stream`.
+ *   x, w_router, logits   as for moe4_route (w_router NULL: logits are given).
+ *   w13, w2               routed expert weights; shared13, shared2 the shared expert
+ *                         (required iff n_shared == 1, else ignored).
+ *   residual, gamma       as for moe4_combine_norm.
+ *   topk_idx, topk_w      int32 / FP32 [T][k] out (the routing decision).
+ *   residual_out, normed_out  BF16 [T][H] out.
+ *   ws                    device workspace of at least moe4_layer_workspace_bytes(shape);
+ *                         it holds the plan, h and y between the steps. */
+moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                       float* logits, const moe4_w4* w13, const moe4_w4* w2,
+                       const moe4_w4* shared13, const moe4_w4* shared2,
+                       const uint16_t* residual, const uint16_t* gamma, int32_t* topk_idx,
+                       float* topk_w, uint16_t* residual_out, uint16_t* normed_out, void* ws,
+                       size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE4_H */

@@ -1,0 +1,123 @@
+"""libmoe4.so loads, exports what include/moe4.h declares, and rejects bad calls
+before touching the GPU (CPU only: every call here fails its argument checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_moe_expert_amd import _lib
+from bit_moe_expert_amd._lib import Shape, W4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe4.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libmoe4.so not built (python -m bit_moe_expert_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ["moe4_route", "moe4_permute", "moe4_expert_ffn", "moe4_combine_norm", "moe4_layer"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_abi_version():
+    assert _lib.load().moe4_abi_version() == 1
+    m = re.search(r"#define MOE4_ABI_VERSION (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == 1
+
+
+def shape(**kw):
+    d = dict(T=8, H=2048, E=128, k=8, I=768, n_shared=0, eps=1e-6)
+    d.update(kw)
+    return Shape(d["T"], d["H"], d["E"], d["k"], d["I"], d["n_shared"], d["eps"])
+
+
+def test_workspace_sizes():
+    lib = _lib.load()
+    s = shape()
+    n = lib.moe4_layer_workspace_bytes(s)
+    pairs, rows = 64, 64
+    assert n >= rows * (768 + 2048) * 2 + 3 * pairs * 4
+    assert lib.moe4_permute_workspace_bytes(s) == 0  # one workgroup for small plans
+    big = shape(T=8192, H=4096, E=128, I=1536)
+    assert lib.moe4_permute_workspace_bytes(big) == (65536 // 4096) * 128 * 4
+    assert lib.moe4_layer_workspace_bytes(shape(H=100)) == 0
+    assert lib.moe4_layer_workspace_bytes(None) == 0
+    sh = shape(T=8192, H=6144, E=160, I=2048, n_shared=1)
+    assert lib.moe4_layer_workspace_bytes(sh) >= (65536 + 8192) * (2048 + 6144) * 2
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails its checks first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=100), _lib.MOE4_ERR_UNSUPPORTED),
+    (dict(H=64), _lib.MOE4_ERR_UNSUPPORTED),
+    (dict(I=96), _lib.MOE4_ERR_UNSUPPORTED),
+    (dict(E=300, k=8), _lib.MOE4_ERR_UNSUPPORTED),
+    (dict(k=17, E=64), _lib.MOE4_ERR_UNSUPPORTED),
+    (dict(k=9, E=8), _lib.MOE4_ERR_UNSUPPORTED),
+    (dict(n_shared=2), _lib.MOE4_ERR_UNSUPPORTED),
+    (dict(T=-1), _lib.MOE4_ERR_INVALID_ARG),
+    (dict(k=0), _lib.MOE4_ERR_INVALID_ARG),
+    (dict(eps=0.0), _lib.MOE4_ERR_INVALID_ARG),
+])
+def test_route_rejects_bad_shapes(kw, status):
+    lib = _lib.load()
+    st = lib.moe4_route(shape(**kw), None, None, FAKE, FAKE, FAKE, None)
+    assert st == status
+    assert lib.moe4_last_error()
+
+
+def test_null_and_misaligned_pointers():
+    lib = _lib.load()
+    s = shape()
+    assert lib.moe4_route(s, None, None, None, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
+    assert b"logits" in lib.moe4_last_error()
+    assert lib.moe4_route(s, FAKE, None, FAKE, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
+    assert lib.moe4_route(s, FAKE + 2, FAKE, FAKE, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
+    assert b"aligned" in lib.moe4_last_error()
+    assert lib.moe4_permute(s, FAKE, None, FAKE, FAKE, None, 0, None) == _lib.MOE4_ERR_INVALID_ARG
+    w = W4(FAKE, FAKE, FAKE)
+    nul = W4(FAKE, None, FAKE)
+    assert lib.moe4_expert_ffn(s, FAKE, FAKE, None, w, w, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
+    assert lib.moe4_expert_ffn(s, FAKE, FAKE, FAKE, w, nul, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
+    assert b"w2.scales" in lib.moe4_last_error()
+    assert lib.moe4_combine_norm(s, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
+    assert b"gamma" in lib.moe4_last_error()
+
+
+def test_permute_workspace_too_small():
+    lib = _lib.load()
+    big = shape(T=8192, H=4096, E=128, I=1536)
+    assert lib.moe4_permute(big, FAKE, FAKE, FAKE, FAKE, None, 0, None) == _lib.MOE4_ERR_WORKSPACE
+    assert lib.moe4_permute(big, FAKE, FAKE, FAKE, FAKE, FAKE, 100, None) == _lib.MOE4_ERR_WORKSPACE
+
+
+def test_layer_workspace_and_shared_checks():
+    lib = _lib.load()
+    s = shape()
+    w = W4(FAKE, FAKE, FAKE)
+    need = lib.moe4_layer_workspace_bytes(s)
+    st = lib.moe4_layer(s, FAKE, None, FAKE, w, w, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, need - 1, None)
+    assert st == _lib.MOE4_ERR_WORKSPACE
+    sh = shape(n_shared=1)
+    st = lib.moe4_layer(sh, FAKE, None, FAKE, w, w, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, 1 << 40, None)
+    assert st == _lib.MOE4_ERR_INVALID_ARG and b"shared13" in lib.moe4_last_error()

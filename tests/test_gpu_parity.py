@@ -1,0 +1,408 @@
+"""HIP path vs the fp64 oracle, through the C ABI (needs an MI355X).
+
+Bars: routing indices, offsets, perm_src and inv bit-exact; routing weights within
+1e-5 (and summing to 1 within 1e-5); layer outputs o and n within 2e-2 * rms(ref)
+as max-abs error. Step-level checks use the tighter bars derived in their docstrings.
+"""
+import dataclasses
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_moe_expert_amd import binding as B
+from bit_moe_expert_amd import workloads as wl
+from tests.gpu_util import (GpuLayer, assert_bf16_close, bf16_f64, condition_router_margin,
+                            rel_rms_err, require_gpu, to_dev, to_host_bits, upload_weights)
+
+pytestmark = pytest.mark.gpu
+
+LAYER_TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ----------------------------------------------------------------------------
+# Route
+# ----------------------------------------------------------------------------
+ROUTE_GIVEN = [
+    ("tiny", None), ("batched_t64", None), ("batched_t256", None), ("prefill", None),
+    ("long_prefill", None),
+    # edge cases: k = 1, k = E, E = 256 with k = 16, ragged T, T = 1
+    ("edge_k1", wl.Workload("edge_k1", T=37, H=128, E=64, k=1, I=128, routing="normal")),
+    ("edge_k_eq_e", wl.Workload("edge_k_eq_e", T=19, H=128, E=16, k=16, I=128, routing="normal")),
+    ("edge_e256_k16", wl.Workload("edge_e256_k16", T=33, H=128, E=256, k=16, I=128, routing="zipf")),
+    ("edge_t1", wl.Workload("edge_t1", T=1, H=128, E=160, k=8, I=128, routing="zipf")),
+]
+
+
+def _logits_only(w: wl.Workload, seed=0):
+    return wl._draw_logits(np.random.SeedSequence([seed, 99]), w, w.T)
+
+
+@pytest.mark.parametrize("name,w", ROUTE_GIVEN, ids=[n for n, _ in ROUTE_GIVEN])
+def test_route_given_logits(name, w):
+    w = wl.workload(name) if w is None else w
+    note(f"route given logits: {name} T={w.T} E={w.E} k={w.k}")
+    L = _logits_only(w)
+    shape = B.make_shape(w.T, w.H, w.E, w.k, w.I)
+    logits = to_dev(L)
+    idx = torch.full((w.T, w.k), -1, dtype=torch.int32, device="cuda")
+    wt = torch.zeros((w.T, w.k), dtype=torch.float32, device="cuda")
+    B.moe4_route(shape, None, None, logits, idx, wt)
+    torch.cuda.synchronize()
+    ref_idx, ref_w = oracle.route(L.astype(np.float64), w.k)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    got_w = wt.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got_w - ref_w)) <= 1e-5
+    assert np.max(np.abs(got_w.sum(axis=1) - 1.0)) <= 1e-5
+
+
+@pytest.mark.parametrize("T", [1, 8, 37, 64])
+def test_route_computed_logits(T):
+    w = wl.workload("decode_t8")
+    note(f"route computed logits: T={T} H={w.H} E={w.E}")
+    inp = wl.make_inputs(w, seed=0, T=T)
+    condition_router_margin(inp)
+    shape = B.make_shape(T, w.H, w.E, w.k, w.I)
+    x, wr = to_dev(inp.x), to_dev(inp.w_router)
+    logits = torch.zeros((T, w.E), dtype=torch.float32, device="cuda")
+    idx = torch.full((T, w.k), -1, dtype=torch.int32, device="cuda")
+    wt = torch.zeros((T, w.k), dtype=torch.float32, device="cuda")
+    B.moe4_route(shape, x, wr, logits, idx, wt)
+    torch.cuda.synchronize()
+    ref_L = oracle.router_logits(inp.x, inp.w_router)
+    got_L = logits.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got_L - ref_L)) < 5e-4  # well inside the 1e-3 margin
+    ref_idx, ref_w = oracle.route(ref_L, w.k)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    assert np.max(np.abs(wt.cpu().numpy() - ref_w)) <= 1e-5
+
+
+# ----------------------------------------------------------------------------
+# Permute
+# ----------------------------------------------------------------------------
+def _idx_case(case, rng):
+    if case == "t1":
+        return rng.permutation(128)[:8][None, :].astype(np.int32), 128
+    if case == "tiny":
+        return rng.integers(0, 8, (16, 2)).astype(np.int32), 8
+    if case == "decode_t8":
+        return np.stack([rng.permutation(128)[:8] for _ in range(8)]).astype(np.int32), 128
+    if case == "batched_t256":
+        return np.stack([rng.permutation(256)[:8] for _ in range(256)]).astype(np.int32), 256
+    if case == "single_max":   # exactly the largest one-workgroup plan
+        return rng.integers(0, 8, (2048, 8)).astype(np.int32), 8
+    if case == "multi_min":    # just past it: three-kernel path, ragged last slice
+        return rng.integers(0, 64, (2049, 8)).astype(np.int32), 64
+    if case == "prefill_zipf":
+        w = wl.workload("prefill")
+        L = _logits_only(w)
+        return oracle.route(L.astype(np.float64), 8)[0], 128
+    if case == "long_zipf":
+        w = wl.workload("long_prefill")
+        L = _logits_only(w)
+        return oracle.route(L.astype(np.float64), 8)[0], 160
+    if case == "one_expert":   # every pair to expert 0 (k = 1)
+        return np.zeros((5000, 1), dtype=np.int32), 32
+    if case == "k_eq_e":
+        return np.stack([rng.permutation(16) for _ in range(100)]).astype(np.int32), 16
+    if case == "sparse_e256":  # most experts empty
+        return rng.choice([3, 200, 255], (3001, 7)).astype(np.int32), 256
+    if case == "t0":
+        return np.zeros((0, 8), dtype=np.int32), 128
+    raise ValueError(case)
+
+
+PERMUTE_CASES = ["t1", "tiny", "decode_t8", "batched_t256", "single_max", "multi_min", "prefill_zipf",
+                 "long_zipf", "one_expert", "k_eq_e", "sparse_e256", "t0"]
+
+
+@pytest.mark.parametrize("case", PERMUTE_CASES)
+def test_permute_bit_exact(case):
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    idx, E = _idx_case(case, rng)
+    T, k = idx.shape
+    note(f"permute: {case} T={T} k={k} E={E}")
+    shape = B.make_shape(T, 128, E, k, 128)
+    d_idx = to_dev(idx) if T else torch.zeros((0, k), dtype=torch.int32, device="cuda")
+    off = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+    perm = torch.full((max(1, T * k),), -7, dtype=torch.int32, device="cuda")
+    inv = torch.full((max(1, T * k),), -7, dtype=torch.int32, device="cuda")
+    nws = B.moe4_permute_workspace_bytes(shape)
+    ws = torch.empty(max(1, nws), dtype=torch.uint8, device="cuda") if nws else None
+    B.moe4_permute(shape, d_idx if T else torch.zeros(1, dtype=torch.int32, device="cuda"), off, perm, inv, ws)
+    torch.cuda.synchronize()
+    r_off, r_perm, r_inv = oracle.permute(idx, E)
+    if T == 0:  # a no-op: nothing written
+        assert np.all(off.cpu().numpy() == -7)
+        return
+    assert np.array_equal(off.cpu().numpy(), r_off)
+    if T:
+        assert np.array_equal(perm.cpu().numpy(), r_perm)
+        assert np.array_equal(inv.cpu().numpy(), r_inv)
+
+
+# ----------------------------------------------------------------------------
+# Expert FFN
+# ----------------------------------------------------------------------------
+FFN_CASES = [
+    ("tiny", None, None),
+    ("decode_t1", None, None),
+    ("decode_t8", None, None),
+    ("batched_t64", None, None),
+    # many rows per expert: several passes of the small-row kernel, ragged tails
+    ("rows_ragged", wl.Workload("rows_ragged", T=301, H=512, E=8, k=2, I=256, routing="zipf"), None),
+    ("prefill_small", wl.Workload("prefill_small", T=1024, H=1024, E=16, k=4, I=384, routing="zipf"), None),
+]
+
+
+def _plan_on_host(inp):
+    L = inp.logits.astype(np.float64) if inp.logits is not None else oracle.router_logits(inp.x, inp.w_router)
+    idx, w = oracle.route(L, inp.w.k)
+    off, perm, inv = oracle.permute(idx, inp.w.E)
+    return idx, w, off, perm, inv
+
+
+@pytest.mark.parametrize("name,w,_", FFN_CASES, ids=[c[0] for c in FFN_CASES])
+def test_expert_ffn_routed(name, w, _):
+    w = wl.workload(name) if w is None else w
+    note(f"expert ffn routed: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
+    inp = wl.make_inputs(w, seed=1)
+    idx, _, off, perm, inv = _plan_on_host(inp)
+    shape = B.make_shape(inp.T, w.H, w.E, w.k, w.I)
+    w13, w2, *_ = upload_weights(inp)
+    R = inp.T * w.k
+    h = torch.zeros((R, w.I), dtype=torch.int16, device="cuda")
+    y = torch.zeros((R, w.H), dtype=torch.int16, device="cuda")
+    B.moe4_expert_ffn(shape, to_dev(inp.x), to_dev(off), to_dev(perm), w13, w2, h, y)
+    torch.cuda.synchronize()
+    got_h, got_y = bf16_f64(h), bf16_f64(y)
+    x = oracle.bf16_value(inp.x)
+    tok = perm // w.k
+    exp_of_row = np.repeat(np.arange(w.E), np.diff(off))
+    ref_h = np.zeros_like(got_h)
+    ref_y = np.zeros_like(got_y)
+    for e in np.unique(exp_of_row):
+        rows = np.flatnonzero(exp_of_row == e)
+        W13 = oracle.dequant(inp.w13.packed[e], inp.w13.scales[e], inp.w13.tscale[e])
+        W2 = oracle.dequant(inp.w2.packed[e], inp.w2.scales[e], inp.w2.tscale[e])
+        ref_h[rows] = oracle.bf16_round(oracle.swiglu_hidden(x[tok[rows]], W13))
+        # down projection checked on the GPU's own h (isolates the second GEMM)
+        ref_y[rows] = oracle.bf16_round(got_h[rows] @ W2.T)
+    assert_bf16_close(got_h, ref_h, "h")
+    assert_bf16_close(got_y, ref_y, "y", slack_rms=2.0 ** -16)
+
+
+def test_expert_ffn_dense_shared():
+    w = wl.Workload("shared_small", T=77, H=1024, E=1, k=1, I=512, routing="normal")
+    note("expert ffn dense (shared expert mode) T=77")
+    inp = wl.make_inputs(w, seed=2)
+    shape = B.make_shape(inp.T, w.H, 1, 1, w.I)
+    w13, w2, *_ = upload_weights(inp)
+    h = torch.zeros((inp.T, w.I), dtype=torch.int16, device="cuda")
+    y = torch.zeros((inp.T, w.H), dtype=torch.int16, device="cuda")
+    B.moe4_expert_ffn(shape, to_dev(inp.x), None, None, w13, w2, h, y)
+    torch.cuda.synchronize()
+    x = oracle.bf16_value(inp.x)
+    W13 = oracle.dequant(inp.w13.packed[0], inp.w13.scales[0], inp.w13.tscale[0])
+    W2 = oracle.dequant(inp.w2.packed[0], inp.w2.scales[0], inp.w2.tscale[0])
+    got_h = bf16_f64(h)
+    assert_bf16_close(got_h, oracle.bf16_round(oracle.swiglu_hidden(x, W13)), "h")
+    assert_bf16_close(bf16_f64(y), oracle.bf16_round(got_h @ W2.T), "y", slack_rms=2.0 ** -16)
+    # end to end against the oracle's FFN (h flips across BF16 boundaries included)
+    assert rel_rms_err(bf16_f64(y), oracle.swiglu_ffn(x, W13, W2)) < 2.0 ** -7
+
+
+@pytest.mark.parametrize("T,H,E,k,I", [(8, 2048, 128, 8, 768), (300, 512, 4, 2, 256)])
+def test_expert_ffn_integer_exact(T, H, E, k, I):
+    """Integer activations in [-4, 4] and power-of-two scales 2^-4..2^0 make every
+    partial sum of g and u a multiple of 2^-5 below 2^18, so FP32 accumulation is
+    exact in any order: h must be within 1 BF16 ulp of silu(g)*u from the exact g, u
+    (the one rounding plus the exp approximation). y is then checked against fp64
+    sums over the GPU's own h: within 1 BF16 ulp plus FP32 accumulation slack."""
+    note(f"expert ffn integer-exact T={T} H={H} E={E}")
+    rng = np.random.default_rng(T + H)
+    w = wl.Workload("intexact", T=T, H=H, E=E, k=k, I=I, routing="normal")
+    inp = wl.make_inputs(w, seed=3)
+    inp.x[:] = wl.to_bf16_bits(rng.integers(-4, 5, (T, H)).astype(np.float64))
+    for m in (inp.w13, inp.w2):
+        m.scales[:] = wl.to_e4m3_codes(np.exp2(rng.integers(-4, 1, m.scales.shape).astype(np.float64)))
+    idx, _, off, perm, inv = _plan_on_host(inp)
+    shape = B.make_shape(T, H, E, k, I)
+    w13, w2, *_ = upload_weights(inp)
+    h = torch.zeros((T * k, I), dtype=torch.int16, device="cuda")
+    y = torch.zeros((T * k, H), dtype=torch.int16, device="cuda")
+    B.moe4_expert_ffn(shape, to_dev(inp.x), to_dev(off), to_dev(perm), w13, w2, h, y)
+    torch.cuda.synchronize()
+    got_h, got_y = bf16_f64(h), bf16_f64(y)
+    x = oracle.bf16_value(inp.x)
+    tok = perm // k
+    exp_of_row = np.repeat(np.arange(E), np.diff(off))
+    for e in np.unique(exp_of_row):
+        rows = np.flatnonzero(exp_of_row == e)
+        W13 = oracle.dequant(inp.w13.packed[e], inp.w13.scales[e], inp.w13.tscale[e])
+        W2 = oracle.dequant(inp.w2.packed[e], inp.w2.scales[e], inp.w2.tscale[e])
+        ref_h = oracle.swiglu_hidden(x[tok[rows]], W13)
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref_h), 1e-30))) - 7)
+        assert np.all(np.abs(got_h[rows] - ref_h) <= ulp * 1.01 + 1e-30), f"expert {e}"
+        ref_y = got_h[rows] @ W2.T
+        ulp_y = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref_y), 1e-30))) - 7)
+        slack = 2.0 ** -20 * np.sqrt(np.mean(ref_y ** 2))
+        assert np.all(np.abs(got_y[rows] - ref_y) <= ulp_y + slack), f"expert {e}"
+
+
+# ----------------------------------------------------------------------------
+# Combine + RMSNorm
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("T,H,k,shared", [(1, 2048, 8, False), (8, 2048, 8, False), (37, 4096, 8, True),
+                                          (16, 256, 2, False), (5, 16384, 16, True)])
+def test_combine_norm(T, H, k, shared):
+    note(f"combine_norm T={T} H={H} k={k} shared={shared}")
+    rng = np.random.default_rng(T * H + k)
+    E = max(k, 16)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    off, perm, inv = oracle.permute(idx, E)
+    y = wl.to_bf16_bits(rng.standard_normal((T * k, H)) * 3)
+    wts = rng.random((T, k)).astype(np.float32)
+    wts /= wts.sum(axis=1, keepdims=True)
+    res = wl.to_bf16_bits(rng.standard_normal((T, H)))
+    gam = wl.to_bf16_bits(rng.uniform(0.5, 1.5, H))
+    sh = wl.to_bf16_bits(rng.standard_normal((T, H))) if shared else None
+    shape = B.make_shape(T, H, E, k, 128)
+    d_res = to_dev(res)
+    out_o = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    out_n = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    B.moe4_combine_norm(shape, to_dev(y), to_dev(inv), to_dev(wts), to_dev(sh) if shared else None,
+                        d_res, to_dev(gam), out_o, out_n)
+    torch.cuda.synchronize()
+    yt = oracle.bf16_value(y)[inv.reshape(T, k)]   # [T, k, H] in token order
+    ref_o, ref_n = oracle.combine_norm(yt, wts.astype(np.float64), res, gam, 1e-6,
+                                       shared=oracle.bf16_value(sh) if shared else None)
+    got_o, got_n = bf16_f64(out_o), bf16_f64(out_n)
+    # one BF16 rounding of an FP32 sum: 2^-8 relative, plus FP32 slack
+    assert np.all(np.abs(got_o - ref_o) <= 2 ** -8 * np.abs(ref_o) + 1e-5 * np.sqrt(np.mean(ref_o ** 2)))
+    assert np.all(np.abs(got_n - ref_n) <= 2 ** -7 * np.abs(ref_n) + 1e-5 * np.sqrt(np.mean(ref_n ** 2)))
+    # in-place: residual_out aliases residual
+    B.moe4_combine_norm(shape, to_dev(y), to_dev(inv), to_dev(wts), to_dev(sh) if shared else None,
+                        d_res, to_dev(gam), d_res, out_n)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(d_res), to_host_bits(out_o))
+
+
+def test_combine_norm_closed_form_zero_experts():
+    """y = 0: o = residual exactly and n = r / rms(r) * gamma."""
+    T, H, k, E = 4, 2048, 8, 128
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    _, _, inv = oracle.permute(idx, E)
+    res = wl.to_bf16_bits(rng.standard_normal((T, H)))
+    gam = wl.to_bf16_bits(rng.uniform(0.5, 1.5, H))
+    shape = B.make_shape(T, H, E, k, 128)
+    out_o = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    out_n = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    wts = np.full((T, k), 1.0 / k, dtype=np.float32)
+    B.moe4_combine_norm(shape, torch.zeros((T * k, H), dtype=torch.int16, device="cuda"), to_dev(inv),
+                        to_dev(wts), None, to_dev(res), to_dev(gam), out_o, out_n)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(out_o), res)
+    r = oracle.bf16_value(res)
+    ref_n = r / np.sqrt(np.mean(r * r, axis=1, keepdims=True) + 1e-6) * oracle.bf16_value(gam)
+    assert np.all(np.abs(bf16_f64(out_n) - ref_n) <= 2 ** -7 * np.abs(ref_n) + 1e-6)
+
+
+# ----------------------------------------------------------------------------
+# Whole layer
+# ----------------------------------------------------------------------------
+LAYER_CASES = [("tiny", None), ("decode_t1", None), ("decode_t8", None), ("batched_t64", None),
+               ("batched_t256", None), ("prefill", 96), ("long_prefill", 24)]
+
+
+@pytest.mark.parametrize("name,sample", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+def test_layer_parity(name, sample):
+    w = wl.workload(name)
+    note(f"layer parity: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} shared={w.n_shared}")
+    inp = wl.make_inputs(w, seed=0, chunk=0)
+    if w.routing == "router":
+        condition_router_margin(inp)
+    g = GpuLayer(inp)
+    g.run()
+    got = g.host()
+    # routing: every token
+    L = inp.logits.astype(np.float64) if inp.logits is not None else oracle.router_logits(inp.x, inp.w_router)
+    ref_idx, ref_w = oracle.route(L, w.k)
+    assert np.array_equal(got["idx"], ref_idx)
+    assert np.max(np.abs(got["w"] - ref_w)) <= 1e-5
+    assert np.max(np.abs(got["w"].sum(axis=1) - 1)) <= 1e-5
+    # outputs: every token, or a seeded sample of them for the prefill shapes
+    tokens = None
+    if sample is not None:
+        tokens = np.sort(np.random.default_rng(123).choice(w.T, sample, replace=False))
+    ref = oracle.layer(inp, tokens=tokens, logits=L if tokens is None else L[tokens])
+    sel = ref["tokens"]
+    e_o = rel_rms_err(got["o"][sel], ref["o"])
+    e_n = rel_rms_err(got["n"][sel], ref["n"])
+    note(f"  rel-rms err o={e_o:.2e} n={e_n:.2e}")
+    assert e_o <= LAYER_TOL and e_n <= LAYER_TOL
+
+
+def test_layer_deterministic_and_batch_independent():
+    w = wl.workload("decode_t8")
+    note("layer determinism / batch independence: decode T=8 vs T=1")
+    inp = wl.make_inputs(w, seed=0)
+    condition_router_margin(inp)
+    g = GpuLayer(inp)
+    g.run()
+    a = g.host()
+    g.run()
+    b = g.host()
+    assert np.array_equal(a["o_bits"], b["o_bits"]) and np.array_equal(a["n_bits"], b["n_bits"])
+    # token 3 alone gives the same bytes as inside the batch of 8
+    one = dataclasses.replace(inp, x=inp.x[3:4].copy(), residual=inp.residual[3:4].copy())
+    g1 = GpuLayer(one, weights=(g.w13, g.w2, None, None, g.w_router))
+    g1.run()
+    c = g1.host()
+    assert np.array_equal(c["idx"][0], a["idx"][3])
+    assert np.array_equal(c["o_bits"][0], a["o_bits"][3])
+    assert np.array_equal(c["n_bits"][0], a["n_bits"][3])
+
+
+def test_layer_t0_is_a_noop():
+    w = wl.workload("tiny")
+    inp = wl.make_inputs(w, seed=0, T=0)
+    g = GpuLayer(inp)
+    g.run()
+    torch.cuda.synchronize()
+
+
+def test_long_prefill_chunks_match_one_call():
+    """Tokens are independent, so four calls of 2 048 tokens equal one call of 8 192
+    on the routing and, up to FP32 summation order, on the outputs."""
+    w = wl.workload("long_prefill")
+    note("long prefill: 4 chunks vs 1 call")
+    inp = wl.make_inputs(w, seed=0, chunk=1)
+    g = GpuLayer(inp)
+    g.run()
+    full = g.host()
+    weights = (g.w13, g.w2, g.shared13, g.shared2, None)
+    for c in range(4):
+        sl = slice(c * 2048, (c + 1) * 2048)
+        part = dataclasses.replace(inp, x=inp.x[sl].copy(), residual=inp.residual[sl].copy(),
+                                   logits=inp.logits[sl].copy())
+        gp = GpuLayer(part, weights=weights)
+        gp.run()
+        got = gp.host()
+        assert np.array_equal(got["idx"], full["idx"][sl])
+        assert rel_rms_err(got["o"], full["o"][sl]) < 1e-2
+        assert rel_rms_err(got["n"], full["n"][sl]) < 1e-2

@@ -36,6 +36,8 @@ _W4 = POINTER(W4)
 SIGNATURES = {
     "moe4_abi_version": (c_int, []),
     "moe4_last_error": (c_char_p, []),
+    "moe4_prepack_w4": (c_int, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_void_p]),
     "moe4_permute_workspace_bytes": (c_size_t, [_SHAPE]),
     "moe4_layer_workspace_bytes": (c_size_t, [_SHAPE]),
     "moe4_route": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),

@@ -42,18 +42,34 @@ def make_shape(T: int, H: int, E: int, k: int, I: int, n_shared: int = 0, eps: f
     return Shape(T, H, E, k, I, n_shared, eps)
 
 
+def moe4_prepack_w4(G: int, N: int, K: int, codes, scales, tcodes, tscales, stream=None) -> None:
+    n = G * N * K
+    check(_lib.load().moe4_prepack_w4(
+        G, N, K, _ptr(codes, "codes", (torch.uint8,), n // 2), _ptr(scales, "scales", (torch.uint8,), n // 16),
+        _ptr(tcodes, "tcodes", (torch.uint8,), n // 2), _ptr(tscales, "tscales", (torch.uint8,), n // 16),
+        _stream(stream)))
+
+
 @dataclass
 class DeviceW4:
-    """A grouped 4-bit weight tensor resident on the GPU."""
-    packed: torch.Tensor   # uint8 [G, N, K/2]
-    scales: torch.Tensor   # uint8 [G, N, K/16]
+    """A grouped 4-bit weight tensor resident on the GPU, in the tiled layout the
+    expert FFN reads (same bytes as the canonical layout, re-laid out once)."""
+    packed: torch.Tensor   # uint8 [G, N, K/2] bytes, tiled
+    scales: torch.Tensor   # uint8 [G, N, K/16] bytes, tiled
     tscale: torch.Tensor   # float32 [G]
 
     @classmethod
     def from_host(cls, w, device="cuda") -> "DeviceW4":
-        return cls(torch.from_numpy(w.packed).to(device),
-                   torch.from_numpy(w.scales).to(device),
-                   torch.from_numpy(w.tscale).to(device))
+        """Upload canonical host weights (packed [G,N,K/2], scales [G,N,K/16]) and tile them."""
+        G, N, K2 = w.packed.shape
+        codes = torch.from_numpy(w.packed).to(device)
+        scales = torch.from_numpy(w.scales).to(device)
+        tcodes = torch.empty_like(codes)
+        tscales = torch.empty_like(scales)
+        moe4_prepack_w4(G, N, 2 * K2, codes, scales, tcodes, tscales)
+        torch.cuda.current_stream().synchronize()
+        del codes, scales
+        return cls(tcodes, tscales, torch.from_numpy(w.tscale).to(device))
 
     def clone(self) -> "DeviceW4":
         return DeviceW4(self.packed.clone(), self.scales.clone(), self.tscale.clone())

@@ -98,6 +98,23 @@ int moe4_abi_version(void) { return MOE4_ABI_VERSION; }
 
 const char* moe4_last_error(void) { return g_err; }
 
+moe4_status moe4_prepack_w4(int32_t G, int32_t N, int32_t K, const uint8_t* codes,
+                            const uint8_t* scales, uint8_t* tcodes, uint8_t* tscales, void* stream) {
+  g_err[0] = 0;
+  if (G < 0 || N < 0 || K < 0) return fail(MOE4_ERR_INVALID_ARG, "negative size (G=%d N=%d K=%d)", G, N, K);
+  if (N % 32 || K % 128)
+    return fail(MOE4_ERR_UNSUPPORTED, "prepack needs N %% 32 == 0 and K %% 128 == 0 (N=%d K=%d)", N, K);
+  if ((long long)G * N * K == 0) return MOE4_OK;
+  NEED(codes, "codes");
+  NEED(tcodes, "tcodes");
+  if (scales == nullptr) return fail(MOE4_ERR_INVALID_ARG, "scales is NULL");
+  if (tscales == nullptr) return fail(MOE4_ERR_INVALID_ARG, "tscales is NULL");
+  hipError_t e = moe4::launch_prepack(codes, scales, G, N, K, tcodes, tscales,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prepack launch");
+  return MOE4_OK;
+}
+
 size_t moe4_permute_workspace_bytes(const moe4_shape* shape) {
   if (check_shape(shape) != MOE4_OK) return 0;
   return moe4::permute_workspace_bytes((long long)shape->T * shape->k, shape->E);
@@ -182,7 +199,7 @@ moe4_status moe4_expert_ffn(const moe4_shape* shape, const uint16_t* x, const in
   hipError_t e = moe4::launch_ffn_up(x, offsets, perm_src, shape->k, shape->T, G, shape->H, shape->I,
                                      view(w13), h, s);
   if (e != hipSuccess) return hip_fail(e, "ffn up launch");
-  e = moe4::launch_ffn_down(h, offsets, shape->T, G, shape->H, shape->I, view(w2), y, s);
+  e = moe4::launch_ffn_down(h, offsets, shape->k, shape->T, G, shape->H, shape->I, view(w2), y, s);
   if (e != hipSuccess) return hip_fail(e, "ffn down launch");
   return MOE4_OK;
 }
@@ -220,7 +237,7 @@ moe4_status moe4_expert_down(const moe4_shape* shape, const uint16_t* h, const i
   if ((st = check_w4(w2, "w2"))) return st;
   NEED(y, "y");
   const int G = offsets ? shape->E : 1;
-  hipError_t e = moe4::launch_ffn_down(h, offsets, shape->T, G, shape->H, shape->I, view(w2), y,
+  hipError_t e = moe4::launch_ffn_down(h, offsets, shape->k, shape->T, G, shape->H, shape->I, view(w2), y,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ffn down launch");
   return MOE4_OK;
@@ -302,7 +319,7 @@ moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_
   if (e != hipSuccess) return hip_fail(e, "permute launch");
   e = moe4::launch_ffn_up(x, offsets, perm_src, k, T, E, H, I, view(w13), h, s);
   if (e != hipSuccess) return hip_fail(e, "ffn up launch");
-  e = moe4::launch_ffn_down(h, offsets, T, E, H, I, view(w2), y, s);
+  e = moe4::launch_ffn_down(h, offsets, k, T, E, H, I, view(w2), y, s);
   if (e != hipSuccess) return hip_fail(e, "ffn down launch");
   const uint16_t* shared_y = nullptr;
   if (shape->n_shared) {
@@ -310,7 +327,7 @@ moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_
     uint16_t* ys = y + pairs * H;
     e = moe4::launch_ffn_up(x, nullptr, nullptr, k, T, 1, H, I, view(shared13), hs, s);
     if (e != hipSuccess) return hip_fail(e, "shared ffn up launch");
-    e = moe4::launch_ffn_down(hs, nullptr, T, 1, H, I, view(shared2), ys, s);
+    e = moe4::launch_ffn_down(hs, nullptr, k, T, 1, H, I, view(shared2), ys, s);
     if (e != hipSuccess) return hip_fail(e, "shared ffn down launch");
     shared_y = ys;
   }

@@ -21,7 +21,11 @@ size_t permute_workspace_bytes(long long n, int E);
 hipError_t launch_permute(const int32_t* idx, long long n, int E, int32_t* offsets, int32_t* perm_src,
                           int32_t* inv, void* ws, hipStream_t s);
 
-// Grouped W4A16 FFN halves.
+// Canonical -> tiled weight layout (lossless).
+hipError_t launch_prepack(const uint8_t* codes, const uint8_t* scales, int G, int N, int K,
+                          uint8_t* tcodes, uint8_t* tscales, hipStream_t s);
+
+// Grouped W4A16 FFN halves; weights in the tiled layout.
 struct W4View {
   const uint8_t* packed;
   const uint8_t* scales;
@@ -31,7 +35,7 @@ struct W4View {
 hipError_t launch_ffn_up(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
                          int T, int G, int H, int I, W4View w13, uint16_t* h, hipStream_t s);
 // y[r] = W2 . h[r]
-hipError_t launch_ffn_down(const uint16_t* h, const int32_t* offsets, int T, int G, int H, int I,
+hipError_t launch_ffn_down(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H, int I,
                            W4View w2, uint16_t* y, hipStream_t s);
 
 // o = residual + sum_j w_j * y[inv[t*k+j]] (+ shared); n = rmsnorm(o) * gamma.

@@ -21,6 +21,16 @@
  *   projection.  W2 (per expert): N = H rows, K = I.  The shared expert uses the same
  *   layouts with one expert.
  *
+ * Weight layouts. The layout above is the canonical (checkpoint) layout. The expert
+ * FFN entry points read the TILED layout that moe4_prepack_w4 produces from it once,
+ * at weight-load time: the same bytes, moved so that every 16-row x 128-column tile
+ * is 1 KB of codes plus 128 B of scales in the order the MFMA operands consume them.
+ * Tile (g, b, s) (expert g, rows 16b..16b+15, columns 128s..128s+127) sits at tile
+ * index (g * N/16 + b) * K/128 + s; within it, lane l = rn + 16*kq (rn = l % 16,
+ * kq = l / 16) owns code bytes 16l..16l+15 = canonical row 16b+rn, columns
+ * 128s+32kq..+31, and scale bytes 2l, 2l+1 = that row's scales for column groups
+ * 8s+2kq and 8s+2kq+1. The tensor scales are not moved.
+ *
  * The expert FFN is SwiGLU: h = silu(gate . x) * (up . x), y = W2 . h.
  * Routing: softmax over the E logits, the k largest selected (ties -> lower expert
  * index, output in descending order), their probabilities renormalised to sum to 1.
@@ -81,7 +91,8 @@ typedef struct {
 } moe4_shape;
 
 /* One grouped 4-bit weight tensor over G experts (host struct of device pointers).
- * packed [G][N][K/2], scales [G][N][K/16], tscale [G]. */
+ * packed: G*N*K/2 code bytes and scales: G*N*K/16 E4M3 bytes, both in the TILED layout
+ * (see moe4_prepack_w4); tscale [G] FP32. */
 typedef struct {
   const uint8_t* packed;
   const uint8_t* scales;
@@ -94,6 +105,16 @@ int moe4_abi_version(void);
 /* Text of the last error on the calling thread ("" if none). Never NULL; owned by the
  * library and valid until the next call on the same thread. */
 const char* moe4_last_error(void);
+
+/* Canonical -> tiled re-layout of one grouped 4-bit tensor (lossless; sizes unchanged).
+ * Not on the per-token path: call once when weights are loaded.
+ *   G, N, K   experts, rows and columns (N % 32 == 0, K % 128 == 0, else
+ *             MOE4_ERR_UNSUPPORTED; G*N*K == 0 is a no-op).
+ *   codes     device [G][N][K/2] canonical codes (16-byte aligned); scales [G][N][K/16].
+ *   tcodes    device out, G*N*K/2 bytes (16-byte aligned); tscales out, G*N*K/16 bytes.
+ * Output buffers must not overlap the inputs. */
+moe4_status moe4_prepack_w4(int32_t G, int32_t N, int32_t K, const uint8_t* codes,
+                            const uint8_t* scales, uint8_t* tcodes, uint8_t* tscales, void* stream);
 
 /* Bytes of workspace moe4_permute needs for `shape` (host, pure; 0 on a bad shape). */
 size_t moe4_permute_workspace_bytes(const moe4_shape* shape);

@@ -121,3 +121,12 @@ def test_layer_workspace_and_shared_checks():
     st = lib.moe4_layer(sh, FAKE, None, FAKE, w, w, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                         FAKE, 1 << 40, None)
     assert st == _lib.MOE4_ERR_INVALID_ARG and b"shared13" in lib.moe4_last_error()
+
+
+def test_prepack_checks():
+    lib = _lib.load()
+    assert lib.moe4_prepack_w4(1, 48, 256, FAKE, FAKE, FAKE, FAKE, None) == _lib.MOE4_ERR_UNSUPPORTED
+    assert lib.moe4_prepack_w4(1, 64, 200, FAKE, FAKE, FAKE, FAKE, None) == _lib.MOE4_ERR_UNSUPPORTED
+    assert lib.moe4_prepack_w4(-1, 64, 256, FAKE, FAKE, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
+    assert lib.moe4_prepack_w4(1, 64, 256, None, FAKE, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
+    assert lib.moe4_prepack_w4(0, 64, 256, None, None, None, None, None) == _lib.MOE4_OK

@@ -92,6 +92,34 @@ LayerWs layer_ws_layout(const moe4_shape* s) {
 
 }  // namespace
 
+namespace moe4 {
+
+// Rows per expert at which the 256-row MFMA tiles of the prefill kernel pay off over
+// streaming each weight tile once per 16 rows.
+constexpr long long kPrefillRowsPerExpert = 64;
+
+static bool use_prefill(const int32_t* offsets, int T, int k, int G, int H, int I) {
+  if (!prefill_shape_ok(H, I)) return false;
+  const long long rows = offsets ? (long long)T * k : T;
+  return rows >= kPrefillRowsPerExpert * (offsets ? G : 1);
+}
+
+hipError_t launch_ffn_up(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
+                         int T, int G, int H, int I, W4View w13, uint16_t* h, hipStream_t s) {
+  if (use_prefill(offsets, T, k, G, H, I))
+    return launch_ffn_up_prefill(x, offsets, perm_src, k, T, G, H, I, w13, h, s);
+  return launch_ffn_up_decode(x, offsets, perm_src, k, T, G, H, I, w13, h, s);
+}
+
+hipError_t launch_ffn_down(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H, int I,
+                           W4View w2, uint16_t* y, hipStream_t s) {
+  if (use_prefill(offsets, T, k, G, H, I))
+    return launch_ffn_down_prefill(h, offsets, k, T, G, H, I, w2, y, s);
+  return launch_ffn_down_decode(h, offsets, k, T, G, H, I, w2, y, s);
+}
+
+}  // namespace moe4
+
 extern "C" {
 
 int moe4_abi_version(void) { return MOE4_ABI_VERSION; }

@@ -138,11 +138,14 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
         load_tile(t, a.tcodes + (tile0 + s) * 1024, a.tcodes + (tile1 + s) * 1024,
                   a.tscales + (tile0 + s) * 128, a.tscales + (tile1 + s) * 128, lane);
     };
+    // rows past the expert's end read a valid row (r0) and are zeroed without a branch
+    const uint32_t xmask = aval ? ~0u : 0u;
     auto load_x = [&](u32x4* xv, int s) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xv[j] = (aval && s < s_end) ? *reinterpret_cast<const u32x4*>(arow + s * 128 + 8 * j)
-                                    : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(arow + s * 128 + 8 * j);
+        xv[j] = u32x4{v[0] & xmask, v[1] & xmask, v[2] & xmask, v[3] & xmask};
+      }
     };
     // close slice `sl`: wave 0 adds it to its running total; other waves hand it over
     auto close_slice = [&](int sl) {
@@ -232,7 +235,7 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
 
 }  // namespace
 
-hipError_t launch_ffn_up(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
+hipError_t launch_ffn_up_decode(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
                          int T, int G, int H, int I, W4View w13, uint16_t* h, hipStream_t s) {
   if (T == 0) return hipSuccess;
   DecodeArgs a{x, offsets, perm_src, k, T, w13.packed, w13.scales, w13.tscale, 2 * I, H, I, 1, h, G, 0};
@@ -240,7 +243,7 @@ hipError_t launch_ffn_up(const uint16_t* x, const int32_t* offsets, const int32_
   return launch(true, a, active, G, s);
 }
 
-hipError_t launch_ffn_down(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H, int I,
+hipError_t launch_ffn_down_decode(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H, int I,
                            W4View w2, uint16_t* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
   DecodeArgs a{h, offsets, nullptr, 1, T, w2.packed, w2.scales, w2.tscale, H, I, I, 1, y, G, 0};

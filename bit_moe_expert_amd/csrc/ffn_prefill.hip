@@ -1,0 +1,314 @@
+// Grouped W4A16 expert FFN for many rows per expert (prefill): an MFMA grouped GEMM.
+//
+// Prefill pushes all prompt tokens through one large matmul and is bound by the
+// matrix units, not by memory (the GB10 bandwidth budget article, section
+// "Mechanism: decode is bandwidth-bound, prefill is compute-bound"); the weights
+// are NVFP4 computed against BF16 activations, i.e. W4A16 (bear-blog article on
+// TensorFold 1.0.12 / PR804, section "NVFP4 is neither uniform 4-bit nor all-FP4
+// compute"). So the 4-bit weights are dequantised exactly into BF16 once per
+// workgroup tile and fed to BF16 MFMAs with FP32 accumulation.
+//
+// Tiling. A workgroup (4 waves) computes a 256-row x 256-column output tile of one
+// expert over K in steps of 64; each wave owns 128 x 128 of it as 4 x 4 blocks of
+// 32x32x16 MFMAs (on gfx950 this shape runs near the BF16 peak, while 16x16x32 tops
+// out near half of it). For the up projection the 256 weight rows are 128 gate rows and
+// the matching 128 up rows, so each wave holds gate and up accumulators of the same
+// h columns in the same lanes and applies SwiGLU in registers.
+//
+// Pipeline. Activation rows (gathered through perm_src for the up projection) and
+// weight half-tiles (tiled layout, 512 contiguous bytes per 16-row block) are loaded
+// into registers two K steps ahead; during step i's MFMAs, step i+1's registers are
+// dequantised (code * E4M3 scale is exact in BF16) and written to the other LDS
+// buffer part by part, each part's registers then refilled with step i+2. One
+// barrier per step. Each 16-wide K substep reads its operand fragments from LDS while
+// the previous one's MFMAs run. LDS rows are XOR-swizzled
+// in 16-byte chunks so the MFMA operand reads spread over the banks.
+//
+// Scheduling. One grid covers (expert M-tile, N-tile) pairs up to a bound; each
+// workgroup finds its expert by scanning the per-expert tile counts from the
+// offsets. Workgroup ids are remapped so each XCD (ids are dealt round-robin to the
+// 8 XCDs) gets a contiguous run of tiles with N fastest: the workgroups sharing an
+// activation tile, and an expert's weights, meet in the same L2.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace moe4 {
+
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+
+struct GemmArgs {
+  const uint16_t* act;      // up: x [T][H]; down: h [R][I]
+  const int32_t* offsets;   // [G+1] or NULL (dense: one group of T rows)
+  const int32_t* perm_src;  // up only: row -> flat pair (token = pair / k); NULL = identity
+  int k;
+  int T;
+  const uint8_t* tcodes;
+  const uint8_t* tscales;
+  const float* tscale;
+  int N, K, I;              // up: N = 2I, K = H; down: N = H, K = I
+  int G;
+  uint16_t* out;            // up: h [R][I]; down: y [R][N]
+  int n_tiles;              // output column tiles per expert
+  int total;                // grid size (multiple of kXcds)
+};
+
+// element offset of (row, 16-byte chunk) in a [rows][64] BF16 LDS tile
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3); }
+
+template <bool kUp>
+__global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BN * BK];
+  __shared__ int sched[3];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // XCD-aware remap of the workgroup id to a logical tile, N fastest
+  const int per_xcd = a.total / kXcds;
+  const int Q = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int mtile = Q / a.n_tiles, nt = Q % a.n_tiles;
+
+  // expert and row range of M-tile `mtile`
+  if (wave == 0) {
+    int g = -1, r0 = 0, M = 0, mt = 0;
+    if (a.offsets) {
+      int carry = 0;
+      for (int base = 0; base < a.G && g < 0; base += 64) {
+        const int e = base + lane;
+        const int cnt = e < a.G ? a.offsets[e + 1] - a.offsets[e] : 0;
+        const int tiles = (cnt + BM - 1) / BM;
+        int incl = tiles;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(incl, off);
+          if (lane >= off) incl += o;
+        }
+        const int excl = carry + incl - tiles;
+        const uint64_t hit = __ballot(e < a.G && tiles > 0 && mtile >= excl && mtile < excl + tiles);
+        if (hit) {
+          const int src = __ffsll((long long)hit) - 1;
+          g = __shfl(e, src);
+          mt = mtile - __shfl(excl, src);
+        }
+        carry += __shfl(incl, 63);
+      }
+      if (g >= 0) {
+        r0 = a.offsets[g];
+        M = a.offsets[g + 1] - r0;
+      }
+    } else {
+      g = 0;
+      M = a.T;
+      mt = mtile;
+      if (mt * BM >= M) g = -1;
+    }
+    if (lane == 0) {
+      sched[0] = g;
+      sched[1] = r0 + mt * BM;  // first row of the tile
+      sched[2] = min(BM, M - mt * BM);
+    }
+  }
+  __syncthreads();
+  const int g = sched[0];
+  if (g < 0 || Q >= a.total) return;
+  const int row0 = sched[1], rows = sched[2];
+
+  const int K = a.K, NS = K / 128, NB = a.N / 16, nsteps = K / BK;
+  const float ts = a.tscale[g];
+
+  // ---- global -> register loads ----
+  // A: thread t loads rows t/8 + 32i (i = 0..7), 16-byte chunk t%8 of the step. Rows
+  // past the tile's end read the tile's first row instead: their results are never
+  // stored, so they need no masking.
+  const int a_chunk = tid & 7;
+  const uint16_t* a_src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rr = (tid >> 3) + 32 * i;
+    int src = row0 + (rr < rows ? rr : 0);
+    if (kUp && a.perm_src) src = a.perm_src[src] / a.k;
+    a_src[i] = a.act + (size_t)src * K + a_chunk * 8;
+  }
+  // B: units u = tid, tid + 256: 16-row block u/32, lane-in-half-tile u%32
+  const uint8_t* b_code[2];
+  const uint8_t* b_scale[2];
+  int b_st[2];  // LDS element offset of the unit's row (its 4 chunks are 4*kq' + j)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int u = tid + 256 * h;
+    const int blk = u >> 5, l = u & 31;
+    int wblk;  // weight row-block of this LDS block
+    if (kUp) wblk = blk < 8 ? (nt * 128) / 16 + blk : (a.I + nt * 128) / 16 + (blk - 8);
+    else wblk = (nt * BN) / 16 + blk;
+    const size_t tile = ((size_t)g * NB + wblk) * NS;
+    b_code[h] = a.tcodes + tile * 1024 + l * 16;
+    b_scale[h] = a.tscales + tile * 128 + l * 2;
+    b_st[h] = blk * 16 + (l & 15);
+  }
+  const int b_kq = (tid & 31) >> 4;  // same for both units
+  // LDS swizzle: the 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7). For every
+  // row a lane touches, (r >> 1) & 7 depends only on the lane, so the addresses are a
+  // per-lane base plus immediate offsets.
+  const int a_sw = ((tid >> 3) >> 1) & 7;
+  const int a_st = (tid >> 3) * BK + ((a_chunk ^ a_sw) << 3);  // + 32*i*BK for row group i
+  const int b_sw = ((tid & 15) >> 1) & 7;
+
+  u32x4 ra[8], rb[2];
+  uint32_t rs[2];
+  // Part q of step st's global loads: activation rows 2q, 2q+1 of this thread and, for
+  // odd q, weight unit q/2 (whose two store parts have then both been written).
+  auto load_part = [&](int st, int q) {
+    const int k0 = st * BK;
+#pragma unroll
+    for (int i = 2 * q; i < 2 * q + 2; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + k0);
+    if (q & 1) {
+      const int h = q >> 1;
+      const size_t toff = (size_t)(st >> 1) * 1024 + (st & 1) * 512;
+      const size_t soff = (size_t)(st >> 1) * 128 + (st & 1) * 64;
+      rb[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b_code[h] + toff));
+      rs[h] = *reinterpret_cast<const uint16_t*>(b_scale[h] + soff);
+    }
+  };
+  // Part q (0..3) of writing the loaded step into LDS buffer `buf`: activation rows
+  // 2q and 2q+1 of this thread, and two of the eight BF16 chunks of weight unit q/2
+  // (dequantised here).
+  auto store_part = [&](int buf, int q) {
+#pragma unroll
+    for (int i = 2 * q; i < 2 * q + 2; ++i)
+      *reinterpret_cast<u32x4*>(&lds_a[buf][a_st + 32 * i * BK]) = ra[i];
+    const int h = q >> 1;
+    const float sc = (q & 1) ? e4m3_to_f32<1>(rs[h]) : e4m3_to_f32<0>(rs[h]);
+#pragma unroll
+    for (int j = 2 * (q & 1); j < 2 * (q & 1) + 2; ++j)
+      *reinterpret_cast<u32x4*>(&lds_b[buf][b_st[h] * BK + (((4 * b_kq + j) ^ b_sw) << 3)]) =
+          dequant8(rb[h][j], sc);
+  };
+
+  // ---- per-wave tile: 128 rows x 128 LDS B rows as 4 x 4 blocks of 32x32x16 MFMAs ----
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r32 = lane & 31, kh = lane >> 5;  // operand row within a 32-block; K half (8 values)
+  // LDS B rows of block j: up = gate rows 64wn + 32j (j < 2) then up rows
+  // 128 + 64wn + 32(j-2); down = rows 128wn + 32j. Row offsets are multiples of 32.
+  int boff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) boff[j] = kUp ? (j < 2 ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2)) : 128 * wn + 32 * j;
+  const int f_sw = (r32 >> 1) & 7;
+  const int fa_base = (128 * wm + r32) * BK, fb_base = r32 * BK;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // operand fragments of one 16-wide K substep
+  u32x4 fa[4], fb[4], na[4], nb[4];
+  auto read_frags = [&](int buf, int ks, u32x4* A, u32x4* Bv) {
+    const int cs = ((2 * ks + kh) ^ f_sw) << 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Bv[j] = *reinterpret_cast<const u32x4*>(&lds_b[buf][fb_base + boff[j] * BK + cs]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const u32x4*>(&lds_a[buf][fa_base + 32 * i * BK + cs]);
+  };
+
+  // Prologue: step 0 into LDS buffer 0, step 1 into the registers.
+#pragma unroll
+  for (int q = 0; q < 4; ++q) load_part(0, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) store_part(0, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) load_part(min(1, nsteps - 1), q);
+  __syncthreads();
+  read_frags(0, 0, fa, fb);
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    const int next2 = min(st + 2, nsteps - 1);  // the last steps reload themselves (never read)
+    // Four 16-wide substeps. In each, the next substep's fragments are read while this
+    // one's MFMAs run; then one part of step st+1 (loaded during step st-1) is written
+    // to the other buffer, and its registers are refilled with step st+2, which thus
+    // has a whole step to arrive.
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) read_frags(buf, ks + 1, na, nb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+      store_part(buf ^ 1, ks);
+      load_part(next2, ks);
+      if (ks + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          fa[i] = na[i];
+          fb[i] = nb[i];
+        }
+      }
+    }
+    __syncthreads();
+    read_frags(buf ^ 1, 0, fa, fb);
+  }
+
+  // ---- epilogue: acc[i][j][r] is row 8(r/4) + 4kh + r%4, column r32 of block (i, j) ----
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tr = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (tr < rows) {
+        const size_t orow = (size_t)(row0 + tr);
+        if (kUp) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = nt * 128 + 64 * wn + 32 * j + r32;
+            a.out[orow * a.I + col] = f32_to_bf16(silu_mul(ts * acc[i][j][r], ts * acc[i][j + 2][r]));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int col = nt * BN + 128 * wn + 32 * j + r32;
+            a.out[orow * a.N + col] = f32_to_bf16(ts * acc[i][j][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch(bool up, GemmArgs a, long long m_tiles, hipStream_t s) {
+  a.n_tiles = up ? a.I / 128 : a.N / BN;
+  const long long tiles = m_tiles * a.n_tiles;
+  a.total = (int)((tiles + kXcds - 1) / kXcds * kXcds);
+  if (up) hipLaunchKernelGGL(ffn_prefill_kernel<true>, dim3(a.total), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(ffn_prefill_kernel<false>, dim3(a.total), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+long long m_tile_bound(const int32_t* offsets, int T, int k, int G) {
+  if (!offsets) return (T + BM - 1) / BM;
+  return ((long long)T * k + BM - 1) / BM + G;  // each expert adds at most one partial tile
+}
+
+}  // namespace
+
+bool prefill_shape_ok(int H, int I) { return H % BN == 0 && I % 128 == 0; }
+
+hipError_t launch_ffn_up_prefill(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
+                                 int T, int G, int H, int I, W4View w13, uint16_t* h, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  GemmArgs a{x, offsets, perm_src, k, T, w13.packed, w13.scales, w13.tscale, 2 * I, H, I, G, h, 0, 0};
+  return launch(true, a, m_tile_bound(offsets, T, k, G), s);
+}
+
+hipError_t launch_ffn_down_prefill(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H,
+                                   int I, W4View w2, uint16_t* y, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  GemmArgs a{h, offsets, nullptr, 1, T, w2.packed, w2.scales, w2.tscale, H, I, I, G, y, 0, 0};
+  return launch(false, a, m_tile_bound(offsets, T, k, G), s);
+}
+
+}  // namespace moe4

@@ -32,11 +32,23 @@ struct W4View {
   const float* tscale;
 };
 // h[r] = silu(gate . x[tok(r)]) * (up . x[tok(r)]); offsets/perm_src NULL = dense (G=1, R=T).
+// y[r] = W2 . h[r]. The dispatchers pick the decode (streaming) or the prefill (GEMM)
+// kernel from the average rows per expert.
 hipError_t launch_ffn_up(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
                          int T, int G, int H, int I, W4View w13, uint16_t* h, hipStream_t s);
-// y[r] = W2 . h[r]
 hipError_t launch_ffn_down(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H, int I,
                            W4View w2, uint16_t* y, hipStream_t s);
+// few rows per expert: stream each touched weight tile once per 16 rows
+hipError_t launch_ffn_up_decode(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
+                                int T, int G, int H, int I, W4View w13, uint16_t* h, hipStream_t s);
+hipError_t launch_ffn_down_decode(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H,
+                                  int I, W4View w2, uint16_t* y, hipStream_t s);
+// many rows per expert: 256 x 256 MFMA tiles (needs H % 256 == 0, I % 128 == 0)
+bool prefill_shape_ok(int H, int I);
+hipError_t launch_ffn_up_prefill(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
+                                 int T, int G, int H, int I, W4View w13, uint16_t* h, hipStream_t s);
+hipError_t launch_ffn_down_prefill(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H,
+                                   int I, W4View w2, uint16_t* y, hipStream_t s);
 
 // o = residual + sum_j w_j * y[inv[t*k+j]] (+ shared); n = rmsnorm(o) * gamma.
 hipError_t launch_combine_norm(const uint16_t* y, const int32_t* inv, const float* w,

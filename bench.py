@@ -47,7 +47,37 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 1 GiB twice with torch (a plain copy of known size, for "
+                         "scaling FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ffn_up_decode_t8_traffic.md")
+KERNEL_SOURCES = {"decode": os.path.join(ROOT, "bit_moe_expert_amd", "csrc", "ffn_decode.hip"),
+                  "prefill": os.path.join(ROOT, "bit_moe_expert_amd", "csrc", "ffn_prefill.hip")}
+
+
+def source_sha(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(config, kernel_source):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary,
+    if it was taken on this workload with the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if line.startswith("machine:"):
+            for kv in line[len("machine:"):].split():
+                k, _, v = kv.partition("=")
+                vals[k] = v
+    if vals.get("config") != config or vals.get("source_sha") != source_sha(kernel_source):
+        return None
+    return int(vals["traffic_bytes"])
 
 
 def log(msg):
@@ -155,6 +185,13 @@ def main():
                      topk_w, res_out, norm_out, ws)
 
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     calls_per_step = chunks
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup * calls_per_step):
@@ -230,7 +267,10 @@ def main():
         achieved = flops / up_mean_s / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
-    roofline.update({"kernel": "ffn_small_m_kernel<up> (W13 dequant-MFMA + SwiGLU)",
+    kind = "decode" if inp.T * w.k < 64 * w.E else "prefill"
+    roofline["traffic"] = measured_traffic(args.config, KERNEL_SOURCES[kind])
+    roofline.update({"kernel": ("ffn_decode_kernel<true>" if kind == "decode" else "ffn_prefill_kernel<true>")
+                               + " (expert up: W13 dequant-MFMA + SwiGLU)",
                      "mean_us": round(up_mean_s * 1e6, 3), "algorithmic_bytes": int(nbytes),
                      "algorithmic_flops": int(flops)})
 

@@ -341,10 +341,15 @@ moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_
     e = moe4::launch_router_logits(x, w_router, logits, T, H, E, s);
     if (e != hipSuccess) return hip_fail(e, "router_logits launch");
   }
-  e = moe4::launch_topk_softmax(logits, topk_idx, topk_w, T, E, k, s);
-  if (e != hipSuccess) return hip_fail(e, "topk_softmax launch");
-  e = moe4::launch_permute(topk_idx, (long long)pairs, E, offsets, perm_src, inv, perm_ws, s);
-  if (e != hipSuccess) return hip_fail(e, "permute launch");
+  if (moe4::route_plan_fits(T, k)) {
+    e = moe4::launch_route_plan(logits, T, E, k, topk_idx, topk_w, offsets, perm_src, inv, s);
+    if (e != hipSuccess) return hip_fail(e, "route_plan launch");
+  } else {
+    e = moe4::launch_topk_softmax(logits, topk_idx, topk_w, T, E, k, s);
+    if (e != hipSuccess) return hip_fail(e, "topk_softmax launch");
+    e = moe4::launch_permute(topk_idx, (long long)pairs, E, offsets, perm_src, inv, perm_ws, s);
+    if (e != hipSuccess) return hip_fail(e, "permute launch");
+  }
   e = moe4::launch_ffn_up(x, offsets, perm_src, k, T, E, H, I, view(w13), h, s);
   if (e != hipSuccess) return hip_fail(e, "ffn up launch");
   e = moe4::launch_ffn_down(h, offsets, k, T, E, H, I, view(w2), y, s);

@@ -21,6 +21,11 @@ size_t permute_workspace_bytes(long long n, int E);
 hipError_t launch_permute(const int32_t* idx, long long n, int E, int32_t* offsets, int32_t* perm_src,
                           int32_t* inv, void* ws, hipStream_t s);
 
+// Top-k + plan in one workgroup for small batches (route_plan_fits(T, k)).
+bool route_plan_fits(int T, int k);
+hipError_t launch_route_plan(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                             int32_t* offsets, int32_t* perm_src, int32_t* inv, hipStream_t s);
+
 // Canonical -> tiled weight layout (lossless).
 hipError_t launch_prepack(const uint8_t* codes, const uint8_t* scales, int G, int N, int K,
                           uint8_t* tcodes, uint8_t* tscales, hipStream_t s);

@@ -10,9 +10,11 @@
 //
 // Small inputs (n <= kSingleMax) use one 1024-thread workgroup for everything;
 // larger ones use three launches: per-slice histograms, a scan over (expert, slice),
-// and a per-slice stable scatter.
+// and a per-slice stable scatter. For small decode batches the layer can also fuse
+// the top-k selection into the one-workgroup plan (route_plan_kernel).
 #include "device.hpp"
 #include "launch.hpp"
+#include "topk.hpp"
 
 namespace moe4 {
 
@@ -23,6 +25,8 @@ constexpr int kWaves = kThreads / kWave;   // 16
 constexpr int kMaxE = 256;
 constexpr long long kSingleMax = 16384;    // one workgroup up to this many pairs
 constexpr int kSlice = 4096;               // pairs per slice in the multi-block path
+constexpr int kRoutePlanMaxPairs = 16384;  // fused top-k + plan: pairs kept in LDS
+constexpr int kRoutePlanMaxTokens = 64;    // ... and at most 4 tokens per wave
 
 // Exclusive scan of v (one value per thread for threads < 256) across the first four
 // waves; returns the exclusive prefix, and the total through *total. Must be called
@@ -82,15 +86,11 @@ __device__ void scatter_round(const int32_t* __restrict__ flat, long long base, 
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) void permute_single_kernel(const int32_t* __restrict__ flat,
-                                                                  int n, int E,
-                                                                  int32_t* __restrict__ offsets,
-                                                                  int32_t* __restrict__ perm_src,
-                                                                  int32_t* __restrict__ inv) {
-  __shared__ int cnt[kMaxE];
-  __shared__ int run[kMaxE];
-  __shared__ int wcnt[kWaves * kMaxE];
-  __shared__ int lds4[4];
+// The whole plan in one workgroup: histogram, scan, stable scatter. `flat` may point
+// to global memory or LDS.
+__device__ void plan_single(const int32_t* flat, int n, int E, int32_t* __restrict__ offsets,
+                            int32_t* __restrict__ perm_src, int32_t* __restrict__ inv, int* cnt, int* run,
+                            int* wcnt, int* lds4) {
   const int tid = threadIdx.x;
   for (int i = tid; i < E; i += kThreads) cnt[i] = 0;
   __syncthreads();
@@ -107,6 +107,47 @@ __global__ __launch_bounds__(kThreads) void permute_single_kernel(const int32_t*
   __syncthreads();
   for (long long base = 0; base < n; base += kThreads)
     scatter_round(flat, base, n, E, run, wcnt, perm_src, inv);
+}
+
+__global__ __launch_bounds__(kThreads) void permute_single_kernel(const int32_t* __restrict__ flat,
+                                                                  int n, int E,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ perm_src,
+                                                                  int32_t* __restrict__ inv) {
+  __shared__ int cnt[kMaxE];
+  __shared__ int run[kMaxE];
+  __shared__ int wcnt[kWaves * kMaxE];
+  __shared__ int lds4[4];
+  plan_single(flat, n, E, offsets, perm_src, inv, cnt, run, wcnt, lds4);
+}
+
+// Top-k of every token (wave w takes tokens w, w + 16, ...) followed by the plan, in
+// one workgroup: one launch instead of two for small batches. The selections are
+// kept in LDS for the plan and written out as the routing outputs.
+__global__ __launch_bounds__(kThreads) void route_plan_kernel(const float* __restrict__ logits, int T,
+                                                              int E, int k, int32_t* __restrict__ idx,
+                                                              float* __restrict__ w,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ perm_src,
+                                                              int32_t* __restrict__ inv) {
+  __shared__ int sidx[kRoutePlanMaxPairs];
+  __shared__ int cnt[kMaxE];
+  __shared__ int run[kMaxE];
+  __shared__ int wcnt[kWaves * kMaxE];
+  __shared__ int lds4[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = wave; t < T; t += kWaves) {
+    int oi;
+    float ow;
+    topk_softmax_row(logits + (size_t)t * E, E, k, oi, ow);
+    if (lane < k) {
+      sidx[t * k + lane] = oi;
+      idx[(size_t)t * k + lane] = oi;
+      w[(size_t)t * k + lane] = ow;
+    }
+  }
+  __syncthreads();
+  plan_single(sidx, T * k, E, offsets, perm_src, inv, cnt, run, wcnt, lds4);
 }
 
 // Slice b = pairs [b*kSlice, min(n, (b+1)*kSlice)); hist[b][e] = its count of expert e.
@@ -169,6 +210,16 @@ size_t permute_workspace_bytes(long long n, int E) {
   if (n <= kSingleMax) return 0;
   const long long nb = (n + kSlice - 1) / kSlice;
   return (size_t)nb * (size_t)E * sizeof(int);
+}
+
+bool route_plan_fits(int T, int k) { return T <= kRoutePlanMaxTokens && T * k <= kRoutePlanMaxPairs; }
+
+hipError_t launch_route_plan(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                             int32_t* offsets, int32_t* perm_src, int32_t* inv, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(route_plan_kernel, dim3(1), dim3(kThreads), 0, s, logits, T, E, k, idx, w, offsets,
+                     perm_src, inv);
+  return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* idx, long long n, int E, int32_t* offsets, int32_t* perm_src,

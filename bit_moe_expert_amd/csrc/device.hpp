@@ -80,6 +80,23 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 // ---------------------------------------------------------------------------
+// Buffer-resource loads: a wave-uniform base and byte range, a per-lane 32-bit offset.
+// Offsets at or past the range read as zero instead of touching memory.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t BufRes;
+constexpr int kBufResFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+__device__ __forceinline__ BufRes make_res(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufResFlags);
+}
+// 16 bytes, streamed past the caches (nt)
+__device__ __forceinline__ u32x4 load_b128_nt(BufRes r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+__device__ __forceinline__ uint32_t load_b16(BufRes r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
 // Misc
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }

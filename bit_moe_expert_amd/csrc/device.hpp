@@ -12,6 +12,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
@@ -62,6 +64,21 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t codes, float s) {
   return r;
 }
 
+// FP16 form of the same: the two E4M3 scales of a dword's low half -> FP16 (exact:
+// E4M3 values lie in FP16's normal range with 4 significant bits), and eight codes
+// times one of them -> eight FP16 weights (exact: at most 6 significant bits, between
+// 2^-10 and 2688). Two instructions per pair of weights instead of four.
+__device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t v) { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false); }
+__device__ __forceinline__ u32x4 dequant8_f16(uint32_t codes, _Float16 s) {
+  const f16x2 ss = {s, s};
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss);
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss);
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss);
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss);
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA wrappers (operand layouts checked on gfx950):
 //  16x16x32 bf16: lane l supplies A[l%16][kslot(l/16, 0..7)], B[kslot(l/16, 0..7)][l%16];
@@ -73,6 +90,10 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t codes, float s) {
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
 }
 __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),

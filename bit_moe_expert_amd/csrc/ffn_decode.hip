@@ -15,12 +15,16 @@
 // up block, so SwiGLU is applied in registers; down: two consecutive W2 blocks) and
 // streams them along K. When the routing leaves too few blocks to fill the chip
 // (ksplit > 1), the K range of a pair is split over ksplit waves of the workgroup,
-// and their partial sums are added in a fixed order through LDS. Empty experts exit
-// at once. Each K step is dequantised exactly into BF16 (code * E4M3 scale has at
-// most 6 significant bits) in registers; the next two steps' tiles are already in
-// flight. More than 16 rows of one expert take further passes over its tiles.
-// When T*k < E, workgroups are launched only for as many experts as can have rows
-// and each finds its expert among the non-empty ones from the offsets.
+// and their partial sums are added in a fixed order through LDS. Each K step is
+// dequantised exactly into BF16 (code * E4M3 scale has at most 6 significant bits)
+// in registers while the next steps' tiles are in flight.
+//
+// Placement. When the grid is resident at once, the (expert, block pair) units are
+// dealt to workgroups with a stride of one round of workgroups (unit = round * C +
+// slot, C = min(workgroups, CUs)), so the units of each dispatch slot, and hence of
+// each CU, differ by at most one whatever the routing; larger grids give each
+// workgroup consecutive units (C = 1). When T*k < E only as many experts as can have rows are laid out and
+// each wave finds its expert among the non-empty ones from the offsets.
 #include <algorithm>
 
 #include "device.hpp"
@@ -43,7 +47,9 @@ struct DecodeArgs {
   int ksplit;               // waves per pair along K: 1, 2 or 4
   uint16_t* out;            // up: h [R][I]; down: y [R][N]
   int G;                    // experts in the weight tensor
-  int compact;              // grid rows index the non-empty experts (T*k < G)
+  int compact;              // units index the non-empty experts (T*k < G)
+  int slots;                // C: workgroups per round of the placement
+  int stage_rows;           // LDS form: activation rows staged (all of act)
 };
 
 constexpr int kSlices = 4;  // fixed K slices (see the accumulation order below)
@@ -62,19 +68,19 @@ struct Stage<true> {
   uint32_t s0, s1;
 };
 
-// The expert a workgroup works on and its rows [r0, r0 + M).
+// The expert of a unit and its rows [r0, r0 + M); M = 0 when there is none.
 struct Group {
   int g, r0, M;
 };
 
-// Grid row j -> group. Compact grids (T*k < G) take the j-th expert (in index order)
-// that has rows, found from one round of loads: lane l looks at experts 4l .. 4l+3
-// (G <= 256), a wave scan of the per-lane counts finds the lane holding the j-th,
-// and that lane's expert and row range are broadcast. M = 0 if there is none.
-__device__ __forceinline__ Group find_group(const DecodeArgs& a) {
-  const int j = blockIdx.y;
-  if (!a.offsets) return Group{0, 0, a.T};
+// Expert slot j -> group. Compact layouts (T*k < G) take the j-th expert (in index
+// order) that has rows, found from one round of loads: lane l looks at experts
+// 4l .. 4l+3 (G <= 256), a wave scan of the per-lane counts finds the lane holding
+// the j-th, and that lane's expert and row range are broadcast.
+__device__ __forceinline__ Group find_group(const DecodeArgs& a, int j) {
+  if (!a.offsets) return j == 0 ? Group{0, 0, a.T} : Group{0, 0, 0};
   if (!a.compact) {
+    if (j >= a.G) return Group{0, 0, 0};
     const int r0 = a.offsets[j];
     return Group{j, r0, a.offsets[j + 1] - r0};
   }
@@ -122,39 +128,69 @@ __device__ __forceinline__ Group find_group(const DecodeArgs& a) {
 // Byte stride of one activation row staged in LDS: 16 bytes of padding shift
 // consecutive rows by four banks, so the 16 rows of an MFMA operand read conflict-free.
 __host__ __device__ constexpr int x_row_stride(int K) { return 2 * K + 16; }
+// LDS of the staged form: rows, then one FP32 scale per row (16-byte multiple)
+__host__ __device__ constexpr size_t x_stage_bytes(int rows, int K) {
+  return (size_t)rows * x_row_stride(K) + (((size_t)rows * 4 + 15) & ~size_t(15));
+}
+
+// Wave-wide maximum of non-negative floats (NaN ignored), wave-uniform.
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xf, 0xf, false)));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
 
 // The kernel. D = K steps in the register ring: while step s is multiplied, steps
 // s+1 .. s+D-1 are in flight. Loads are never skipped (past the end they re-read the
 // last step), so the number of loads in flight is the same on every path and the
 // compiler's wait counts stay at D-1 stages.
 //
-// kXLds: the workgroup first copies its rows' activations (rows_alloc rows x K) into
-// LDS and the waves read their MFMA operand from there; this frees the 16 registers
-// per stage that the fragment otherwise takes, so more weight tiles are in flight.
-// It is used when the rows of a pass fit in a few tens of KB of LDS (decode batches).
+// kXLds: the workgroup first copies all of `act` (stage_rows rows x K: the batch's
+// tokens for up, all routed rows for down) into LDS and the waves read their MFMA
+// operand from there; this frees the 16 registers per stage that the fragment
+// otherwise takes, so more weight tiles are in flight, and lets the waves of one
+// workgroup work on different experts. Used when that fits a few tens of KB.
+// This form also multiplies in FP16, which halves the dequantisation work (the
+// kernel is close to bound by it): the staged rows are scaled by a power of two each
+// (max |x| below 2^15) and converted to FP16, the weights are exact in FP16 (see
+// dequant8_f16), and the FP32 outputs are scaled back. Scaling by a power of two
+// scales every FP32 partial sum exactly, so the result has the same bits as the BF16
+// form as long as a row's values lie within 2^32 of its maximum (smaller ones round
+// to FP16 subnormals, a change below 2^-40 of the row's largest term).
 template <bool kUp, int D, bool kXLds>
-__global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a,
-                                                                                      int rows_alloc) {
+__global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const Group grp = find_group(a);
-  const int g = grp.g, r0 = grp.r0, M = grp.M;
-  if (M <= 0) return;
-
+  __shared__ int s_npass;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar registers)
   const int rn = lane & 15, kq = lane >> 4;
-  const int ksplit = a.ksplit, pairs = 4 / ksplit;
-  const int p = wave / ksplit, q = wave % ksplit;
+  const int ksplit = a.ksplit, groups = 4 / ksplit;
+  const int gi = wave / ksplit, q = wave % ksplit;
   const int K = a.K, NS = K / 128, NB = a.N / 16;
+  const int pairs_per_group = kUp ? a.I / 16 : a.N / 32;
+  // this wave group's unit: spread over dispatch slots (see Placement)
+  const int b = blockIdx.x, C = a.slots;
+  const int unit = ((b / C) * groups + gi) * C + (b % C);
+  const Group grp = find_group(a, unit / pairs_per_group);
+  const int g = grp.g, r0 = grp.r0, M = grp.M;
+  const int pair = unit % pairs_per_group;
+  const int npass = (M + 15) / 16;
+
   // the pair's two blocks (row-block indices within the expert)
   int b0, b1, col0;
   if (kUp) {
-    col0 = (blockIdx.x * pairs + p) * 16;  // h columns col0..col0+15
-    b0 = col0 / 16;
+    col0 = pair * 16;  // h columns col0..col0+15
+    b0 = pair;
     b1 = (a.I + col0) / 16;
   } else {
-    col0 = (blockIdx.x * pairs + p) * 32;  // y columns col0..col0+31
-    b0 = col0 / 16;
+    col0 = pair * 32;  // y columns col0..col0+31
+    b0 = 2 * pair;
     b1 = b0 + 1;
   }
   const size_t tile0 = ((size_t)g * NB + b0) * NS, tile1 = ((size_t)g * NB + b1) * NS;
@@ -169,131 +205,185 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a,
   // depend on ksplit, i.e. on how many tokens share the call.
   const int nsl = kSlices / ksplit, first = q * nsl;
   const int s_begin = first * NS / kSlices, s_end = (first + nsl) * NS / kSlices;
-  const float ts = a.tscale[g];
   const int xs = x_row_stride(K);
-  // slices of waves q > 0 handed to wave 0: [pairs][kSlices - nsl][2][64] float4,
+  // slices of waves q > 0 handed to wave 0: [groups][kSlices - nsl][2][64] float4,
   // after the staged activations when those are in LDS
-  float4* red = reinterpret_cast<float4*>(smem + (kXLds ? (size_t)rows_alloc * xs : 0));
-  const int rows_per_pass = kXLds ? rows_alloc : 16;
+  float4* red = reinterpret_cast<float4*>(smem + (kXLds ? x_stage_bytes(a.stage_rows, K) : 0));
+  float* row_scale = reinterpret_cast<float*>(smem + (size_t)a.stage_rows * xs);  // LDS form
 
-  for (int pass = 0; pass < M; pass += rows_per_pass) {
-    const int nr = min(rows_per_pass, M - pass);  // real rows in this pass
-    // rows past the pass's real rows use the pass's first row: MFMA rows are
-    // independent and those rows are not stored
-    const int m = rn < nr ? rn : 0;
-
-    Stage<kXLds> st[D];
-    const uint16_t* arow = nullptr;
-    if (!kXLds) {
-      const int r = r0 + pass + m;
-      const int src = kUp && a.perm_src ? a.perm_src[r] / a.k : r;
-      arow = a.act + (size_t)src * K + kq * 32;
-    }
-    // steps past the wave's range re-read its last step; a wave with an empty range
-    // (NS < kSlices) reads step 0 and never uses it: every wave issues the same loads,
-    // so the wait counts after them do not depend on the path taken
-    auto issue = [&](Stage<kXLds>& t, int s) {
-      s = s < s_end ? s : s_end - 1;
-      s = s > 0 ? s : 0;
-      const int co = s * 1024 + lane * 16, so = s * 128 + lane * 2;
-      t.c0 = load_b128_nt(rc0, co);
-      t.c1 = load_b128_nt(rc1, co);
-      t.s0 = load_b16(rs0, so);
-      t.s1 = load_b16(rs1, so);
-      if constexpr (!kXLds) {
+  Stage<kXLds> st[D];
+  const uint16_t* arow = nullptr;
+  // steps past the wave's range re-read its last step; a wave with an empty range
+  // (NS < kSlices) reads step 0 and never uses it: every wave issues the same loads,
+  // so the wait counts after them do not depend on the path taken
+  auto issue = [&](Stage<kXLds>& t, int s) {
+    s = s < s_end ? s : s_end - 1;
+    s = s > 0 ? s : 0;
+    const int co = s * 1024 + lane * 16, so = s * 128 + lane * 2;
+    t.c0 = load_b128_nt(rc0, co);
+    t.c1 = load_b128_nt(rc1, co);
+    t.s0 = load_b16(rs0, so);
+    t.s1 = load_b16(rs1, so);
+    if constexpr (!kXLds) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) t.x[j] = *reinterpret_cast<const u32x4*>(arow + s * 128 + 8 * j);
-      }
-    };
-    // lane i < 16 loads the source row of pass row i first: loads complete in issue
-    // order, so this one does not wait behind the weight tiles issued next
-    int row_src = 0;
-    if (kXLds && lane < 16) {
-      const int r = r0 + pass + (lane < nr ? lane : 0);
-      row_src = kUp && a.perm_src ? a.perm_src[r] : r;
+      for (int j = 0; j < 4; ++j) t.x[j] = *reinterpret_cast<const u32x4*>(arow + s * 128 + 8 * j);
     }
+  };
+  // this lane's activation row in pass `pass`: its token (up: the routed pair's
+  // index, divided by k by row_src) or its routed row (down); rows past the pass's
+  // real rows use the pass's first row (MFMA rows are independent and those rows are
+  // not stored)
+  auto row_pair = [&](int pass) {
+    const int nr = min(16, M - pass * 16);
+    const int r = r0 + pass * 16 + (rn < nr ? rn : 0);
+    return kUp && a.perm_src ? a.perm_src[r] : r;
+  };
+  auto row_src = [&](int pair_or_row) { return kUp && a.perm_src ? pair_or_row / a.k : pair_or_row; };
+  // LDS form: pass 0's row index, then its first tiles go out before the
+  // workgroup-wide activation copy below, so the three round trips overlap (the
+  // index is only used, and so only waited for, after the copy)
+  int src = 0, pair0 = 0;
+  if (kXLds && npass > 0) {
+    pair0 = row_pair(0);
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) issue(st[i], s_begin + i);
-    const bool has_steps = s_begin < s_end;
-    if constexpr (kXLds) {
-      // stage rows pass .. pass+nr-1 of the expert: row i of LDS <- its source row
-      if (kUp && a.perm_src) row_src /= a.k;  // pair index -> token
-      if (pass > 0) __syncthreads();  // the previous pass's reads are done
-      const int cpr = K / 8;           // 16-byte chunks per row
-      const int total = nr * cpr;
-      for (int base = 0; base < total; base += 8 * 256) {
-        u32x4 buf[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int c = base + u * 256 + tid;
-          const int row = c < total ? c / cpr : 0, col = c < total ? c % cpr : 0;
-          const int sr = __shfl(row_src, row);
-          buf[u] = reinterpret_cast<const u32x4*>(a.act + (size_t)sr * K)[col];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int c = base + u * 256 + tid;
-          if (c < total) *reinterpret_cast<u32x4*>(smem + (size_t)(c / cpr) * xs + (c % cpr) * 16) = buf[u];
-        }
-      }
-      __syncthreads();
-    }
-    const uint8_t* xl = smem + (size_t)m * xs + kq * 64;  // this lane's LDS operand row
+  }
 
-    // acc: the running slice; tot: slices first..current, summed in order (wave q = 0)
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, tot0 = acc0, tot1 = acc0;
-    auto compute = [&](const Stage<kXLds>& t, int s) {
-      u32x4 xv[4];
-      if constexpr (kXLds) {
+  // passes of the workgroup: the most of its groups (the K-split hand-over below is
+  // a workgroup barrier, so every wave runs the same number of passes)
+  if (tid == 0) s_npass = 0;
+  __syncthreads();
+  if (lane == 0 && q == 0 && npass > 0) atomicMax(&s_npass, npass);
+  if constexpr (kXLds) {
+    // all rows of act -> LDS rows of x_row_stride(K) bytes
+    const int cpr = K / 8;  // 16-byte chunks per row
+    const int total = a.stage_rows * cpr;
+    auto copy8 = [&](int base) {  // 8 chunks per thread: all loads, then all stores
+      u32x4 buf[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const u32x4*>(xl + s * 256 + 16 * j);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xv[j] = t.x[j];
+      for (int u = 0; u < 8; ++u) {
+        const int c = base + u * 256 + tid;
+        buf[u] = reinterpret_cast<const u32x4*>(a.act)[c < total ? c : 0];
       }
-      const float sa0 = e4m3_to_f32<0>(t.s0), sa1 = e4m3_to_f32<1>(t.s0);
-      const float sb0 = e4m3_to_f32<0>(t.s1), sb1 = e4m3_to_f32<1>(t.s1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc0 = mfma16x16x32(xv[j], dequant8(t.c0[j], j < 2 ? sa0 : sa1), acc0);
-        acc1 = mfma16x16x32(xv[j], dequant8(t.c1[j], j < 2 ? sb0 : sb1), acc1);
+      for (int u = 0; u < 8; ++u) {
+        const int c = base + u * 256 + tid;
+        if (c < total) *reinterpret_cast<u32x4*>(smem + (size_t)(c / cpr) * xs + (c % cpr) * 16) = buf[u];
       }
     };
-    // close slice `sl`: wave 0 adds it to its running total; other waves hand it over
-    auto close_slice = [&](int sl) {
-      if (q == 0) {
-        tot0 += acc0;
-        tot1 += acc1;
-      } else {
-        float4* r = red + ((size_t)(p * (kSlices - nsl) + (sl - nsl)) * 2) * 64;
-        r[lane] = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
-        r[64 + lane] = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
-      }
-      acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc1 = acc0;
-    };
-    int sl = first;
-    if (has_steps) {
-      while (sl < first + nsl && (sl + 1) * NS / kSlices <= s_begin) close_slice(sl++);  // empty slices
-      for (int sb = s_begin; sb < s_end; sb += D) {
+    // the first round outside the loop: a loop head would wait for every load in
+    // flight (the tiles above included) before reusing its registers
+    copy8(0);
+    for (int base = 8 * 256; base < total; base += 8 * 256) copy8(base);
+    __syncthreads();
+    // BF16 -> FP16 in place, row by row (wave w takes rows w, w+4, ...): scale each row
+    // by 2^-sh so that its max |x| is below 2^15, and keep 2^sh for the outputs
+    for (int row = wave; row < a.stage_rows; row += 4) {
+      uint8_t* rp = smem + (size_t)row * xs;
+      float mx = 0.f;
+      for (int c = lane; c < cpr; c += 64) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(rp + c * 16);
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
-          issue(st[(i + D - 1) % D], sb + i + D - 1);
-          if (sb + i < s_end) {
-            compute(st[i], sb + i);
-            // close every slice that ends here (a slice is empty when NS < 4)
-            while (sl < first + nsl && (sl + 1) * NS / kSlices <= sb + i + 1) close_slice(sl++);
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[e])), fabsf(bf16_hi(v[e]))));
+      }
+      mx = wave_max_f32(mx);
+      int sh = __builtin_amdgcn_frexp_expf(mx) - 15;  // mx < 2^(sh + 15)
+      sh = sh < -100 ? -100 : (sh > 100 ? 100 : sh);
+      const float down = __builtin_ldexpf(1.0f, -sh);
+      for (int c = lane; c < cpr; c += 64) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(rp + c * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f16x2 h = {(_Float16)(bf16_lo(v[e]) * down), (_Float16)(bf16_hi(v[e]) * down)};
+          v[e] = __builtin_bit_cast(uint32_t, h);
+        }
+        *reinterpret_cast<u32x4*>(rp + c * 16) = v;
+      }
+      if (lane == 0) row_scale[row] = __builtin_ldexpf(1.0f, sh);
+    }
+  }
+  __syncthreads();
+  const int npass_wg = s_npass;
+  if (npass_wg == 0) return;  // workgroup-uniform
+  if (kXLds) src = row_src(pair0);
+  const float ts = M > 0 ? a.tscale[g] : 0.f;
+
+  for (int pass = 0; pass < npass_wg; ++pass) {
+    const bool active = pass < npass;  // wave-group-uniform
+    const int nr = active ? min(16, M - pass * 16) : 0;  // real rows in this pass
+    f32x4 tot0 = {0.f, 0.f, 0.f, 0.f}, tot1 = tot0;
+    if (active) {
+      if (!kXLds || pass > 0) {  // the LDS form primed pass 0 before the activation copy
+        src = row_src(row_pair(pass));
+        arow = a.act + (size_t)src * K + kq * 32;
+#pragma unroll
+        for (int i = 0; i < D - 1; ++i) issue(st[i], s_begin + i);
+      }
+      const uint8_t* xl = smem + (size_t)src * xs + kq * 64;
+      // acc: the running slice; tot: slices first..current, summed in order (wave q = 0)
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+      auto compute = [&](const Stage<kXLds>& t, int s) {
+        u32x4 xv[4];
+        if constexpr (kXLds) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const u32x4*>(xl + s * 256 + 16 * j);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xv[j] = t.x[j];
+        }
+        if constexpr (kXLds) {
+          const f16x2 sa = e4m3x2_to_f16(t.s0), sb = e4m3x2_to_f16(t.s1);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc0 = mfma16x16x32_f16(xv[j], dequant8_f16(t.c0[j], j < 2 ? sa[0] : sa[1]), acc0);
+            acc1 = mfma16x16x32_f16(xv[j], dequant8_f16(t.c1[j], j < 2 ? sb[0] : sb[1]), acc1);
+          }
+        } else {
+          const float sa0 = e4m3_to_f32<0>(t.s0), sa1 = e4m3_to_f32<1>(t.s0);
+          const float sb0 = e4m3_to_f32<0>(t.s1), sb1 = e4m3_to_f32<1>(t.s1);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc0 = mfma16x16x32(xv[j], dequant8(t.c0[j], j < 2 ? sa0 : sa1), acc0);
+            acc1 = mfma16x16x32(xv[j], dequant8(t.c1[j], j < 2 ? sb0 : sb1), acc1);
+          }
+        }
+      };
+      // close slice `sl`: wave 0 adds it to its running total; other waves hand it over
+      auto close_slice = [&](int sl) {
+        if (q == 0) {
+          tot0 += acc0;
+          tot1 += acc1;
+        } else {
+          float4* r = red + ((size_t)(gi * (kSlices - nsl) + (sl - nsl)) * 2) * 64;
+          r[lane] = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
+          r[64 + lane] = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
+        }
+        acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc1 = acc0;
+      };
+      int sl = first;
+      if (s_begin < s_end) {
+        while (sl < first + nsl && (sl + 1) * NS / kSlices <= s_begin) close_slice(sl++);  // empty slices
+        for (int sb = s_begin; sb < s_end; sb += D) {
+#pragma unroll
+          for (int i = 0; i < D; ++i) {
+            issue(st[(i + D - 1) % D], sb + i + D - 1);
+            if (sb + i < s_end) {
+              compute(st[i], sb + i);
+              // close every slice that ends here (a slice is empty when NS < 4)
+              while (sl < first + nsl && (sl + 1) * NS / kSlices <= sb + i + 1) close_slice(sl++);
+            }
           }
         }
       }
+      while (sl < first + nsl) close_slice(sl++);
     }
-    while (sl < first + nsl) close_slice(sl++);
 
     if (ksplit > 1) {
       __syncthreads();
-      if (q == 0) {
+      if (active && q == 0) {
         for (int w = nsl; w < kSlices; ++w) {  // the other waves' slices, in order
-          const float4* r = red + ((size_t)(p * (kSlices - nsl) + (w - nsl)) * 2) * 64;
+          const float4* r = red + ((size_t)(gi * (kSlices - nsl) + (w - nsl)) * 2) * 64;
           const float4 u0 = r[lane], u1 = r[64 + lane];
           tot0[0] += u0.x; tot0[1] += u0.y; tot0[2] += u0.z; tot0[3] += u0.w;
           tot1[0] += u1.x; tot1[1] += u1.y; tot1[2] += u1.z; tot1[3] += u1.w;
@@ -301,12 +391,20 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a,
       }
       __syncthreads();
     }
-    if (q == 0) {
+    if (active && q == 0) {
       const int mbase = 4 * kq;  // pass rows mbase..mbase+3, column rn
+      if constexpr (kXLds) {  // undo the rows' FP16 scaling (exact: powers of two)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sc = row_scale[__shfl(src, mbase + i)];  // lane mbase+i reads row mbase+i
+          tot0[i] *= sc;
+          tot1[i] *= sc;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (mbase + i < nr) {
-          const size_t row = (size_t)(r0 + pass + mbase + i);
+          const size_t row = (size_t)(r0 + pass * 16 + mbase + i);
           if (kUp) {
             a.out[row * a.I + col0 + rn] = f32_to_bf16(silu_mul(ts * tot0[i], ts * tot1[i]));
           } else {
@@ -339,18 +437,18 @@ int cu_count() {
   return cached;
 }
 
-hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int G, hipStream_t s) {
+// rows: routed rows R (T*k, or T when dense); stage_rows: rows of `act`
+hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int G, int stage_rows,
+                  hipStream_t s) {
   DecodeArgs a = base;
   a.G = G;
-  // when fewer experts can have rows than exist, one grid row per possible one
+  // when fewer experts can have rows than exist, units only for as many as can
   a.compact = active_groups < G;
   const long long pairs_per_group = up ? a.I / 16 : a.N / 32;
   const long long pairs = active_groups * pairs_per_group;
-  // staged rows: at most T (a token sends one row to an expert unless the caller's
-  // routing repeats experts, which only adds passes)
-  const int rows_alloc = a.T < 16 ? a.T : 16;
-  const size_t x_bytes = (size_t)rows_alloc * x_row_stride(a.K);
+  const size_t x_bytes = x_stage_bytes(stage_rows, a.K);
   const bool use_lds = x_bytes <= kXLdsMaxBytes;
+  a.stage_rows = use_lds ? stage_rows : 0;
   // K split: the most waves per pair for which the whole grid is resident at once,
   // so that every wave starts in the first wave of dispatch and no second, partial
   // round of waves trails behind (a wave's lifetime is a few memory latencies)
@@ -358,11 +456,12 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
     const size_t red = ks > 1 ? (size_t)(4 / ks) * (kSlices - kSlices / ks) * 2 * 64 * 16 : 0;
     return (use_lds ? x_bytes : 0) + red;
   };
+  const int cus = cu_count();
   auto resident_waves = [&](int ks) {
     const size_t lds = lds_bytes(ks);
     long long wg_per_cu = kWavesPerSimd;  // 4 waves per workgroup, one per SIMD
     if (lds > 0) wg_per_cu = std::min<long long>(wg_per_cu, (long long)(kLdsPerCu / lds));
-    return (long long)cu_count() * wg_per_cu * 4;
+    return (long long)cus * wg_per_cu * 4;
   };
   int ks = 1;
   for (int cand : {4, 2}) {
@@ -372,15 +471,23 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
     }
   }
   a.ksplit = ks;
-  const int per_wg = 4 / ks;
-  dim3 grid((unsigned)(pairs_per_group / per_wg), (unsigned)(a.compact ? active_groups : G));
+  const long long groups_per_wg = 4 / ks;
+  const long long wgs = (pairs + groups_per_wg - 1) / groups_per_wg;
+  // a whole number of rounds of `slots` workgroups, so that unit <-> (workgroup,
+  // group) is one to one. The spread placement is for grids that are resident at
+  // once; larger ones keep consecutive units (the same expert's pairs, whose rows
+  // the workgroup's waves share in cache) together (slots = 1).
+  const bool one_round = pairs * ks <= resident_waves(ks);
+  const long long slots = one_round ? std::min<long long>(wgs, cus) : 1;
+  a.slots = (int)slots;
+  const long long grid = (wgs + slots - 1) / slots * slots;
   const unsigned lds = (unsigned)lds_bytes(ks);
   if (use_lds) {
-    if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesLds, true>), grid, dim3(256), lds, s, a, rows_alloc);
-    else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesLds, true>), grid, dim3(256), lds, s, a, rows_alloc);
+    if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesLds, true>), dim3((unsigned)grid), dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesLds, true>), dim3((unsigned)grid), dim3(256), lds, s, a);
   } else {
-    if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesReg, false>), grid, dim3(256), lds, s, a, 16);
-    else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesReg, false>), grid, dim3(256), lds, s, a, 16);
+    if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesReg, false>), dim3((unsigned)grid), dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesReg, false>), dim3((unsigned)grid), dim3(256), lds, s, a);
   }
   return hipGetLastError();
 }
@@ -390,17 +497,19 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
 hipError_t launch_ffn_up_decode(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
                          int T, int G, int H, int I, W4View w13, uint16_t* h, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  DecodeArgs a{x, offsets, perm_src, k, T, w13.packed, w13.scales, w13.tscale, 2 * I, H, I, 1, h, G, 0};
+  DecodeArgs a{x, offsets, perm_src, k, T, w13.packed, w13.scales, w13.tscale, 2 * I, H, I, 1, h, G, 0, 1, 0};
   const long long active = offsets ? std::min<long long>((long long)T * k, G) : 1;
-  return launch(true, a, active, G, s);
+  return launch(true, a, active, offsets ? G : 1, T, s);
 }
 
 hipError_t launch_ffn_down_decode(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H, int I,
                            W4View w2, uint16_t* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  DecodeArgs a{h, offsets, nullptr, 1, T, w2.packed, w2.scales, w2.tscale, H, I, I, 1, y, G, 0};
+  DecodeArgs a{h, offsets, nullptr, 1, T, w2.packed, w2.scales, w2.tscale, H, I, I, 1, y, G, 0, 1, 0};
+  const long long rows = offsets ? (long long)T * k : T;
   const long long active = offsets ? std::min<long long>((long long)T * k, G) : 1;
-  return launch(false, a, active, G, s);
+  const int stage_rows = rows <= (1 << 20) ? (int)rows : (1 << 20);
+  return launch(false, a, active, offsets ? G : 1, stage_rows, s);
 }
 
 }  // namespace moe4

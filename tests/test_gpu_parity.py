@@ -69,6 +69,30 @@ def test_route_given_logits(name, w):
     assert np.max(np.abs(got_w.sum(axis=1) - 1.0)) <= 1e-5
 
 
+@pytest.mark.parametrize("E,k", [(8, 1), (8, 8), (128, 8), (256, 16), (160, 3)])
+def test_route_ties_and_special_values(E, k):
+    """Exact ties (lower index wins), -0 equal to +0, -inf logits: indices bit-exact."""
+    note(f"route ties/special values: E={E} k={k}")
+    rng = np.random.default_rng(1234 + E * 17 + k)
+    T = 64
+    vals = np.array([-2.0, -1.0, -0.0, 0.0, 0.5, 1.0, -np.inf], dtype=np.float32)
+    L = vals[rng.integers(0, vals.size, size=(T, E))]
+    L[0, :] = 0.25                                          # all equal
+    L[1, :] = np.where(np.arange(E) % 2 == 0, -0.0, 0.0)    # signed zeros only
+    L[2, :] = -np.inf
+    L[2, E - 1] = 3.0                                       # one finite logit at the end
+    L[3, :] = np.float32(1e30) * np.where(np.arange(E) % 3 == 0, 1.0, -1.0)
+    shape = B.make_shape(T, 128, E, k, 128)
+    idx = torch.full((T, k), -1, dtype=torch.int32, device="cuda")
+    wt = torch.zeros((T, k), dtype=torch.float32, device="cuda")
+    B.moe4_route(shape, None, None, to_dev(L), idx, wt)
+    torch.cuda.synchronize()
+    ref_idx, ref_w = oracle.route(L.astype(np.float64), k)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    got_w = wt.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got_w - ref_w)) <= 1e-5
+
+
 @pytest.mark.parametrize("T", [1, 8, 37, 64])
 def test_route_computed_logits(T):
     w = wl.workload("decode_t8")

@@ -54,16 +54,28 @@ struct DecodeArgs {
 
 constexpr int kSlices = 4;  // fixed K slices (see the accumulation order below)
 
+// Where a wave's MFMA activation operand comes from.
+enum XMode {
+  kXRegs = 0,    // global memory, loaded into registers with each K step
+  kXAll = 1,     // LDS: all rows of `act`, staged once per workgroup
+  kXExpert = 2,  // LDS: the rows of the workgroup's expert, staged per pass
+};
+
 // One K step of a wave: its two 16 x 128 weight tiles and, when the activations are
 // not staged in LDS, its activation fragment.
-template <bool kXLds>
+template <int kX>
 struct Stage {
   u32x4 c0, c1;     // codes of the two blocks (this lane's 16 bytes of each 1 KB tile)
   uint32_t s0, s1;  // two E4M3 scales per block (low half of the loaded dword)
   u32x4 x[4];       // activation row rn, columns 128s + 32kq .. +31
 };
 template <>
-struct Stage<true> {
+struct Stage<kXAll> {
+  u32x4 c0, c1;
+  uint32_t s0, s1;
+};
+template <>
+struct Stage<kXExpert> {
   u32x4 c0, c1;
   uint32_t s0, s1;
 };
@@ -151,20 +163,22 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 // last step), so the number of loads in flight is the same on every path and the
 // compiler's wait counts stay at D-1 stages.
 //
-// kXLds: the workgroup first copies all of `act` (stage_rows rows x K: the batch's
-// tokens for up, all routed rows for down) into LDS and the waves read their MFMA
-// operand from there; this frees the 16 registers per stage that the fragment
-// otherwise takes, so more weight tiles are in flight, and lets the waves of one
-// workgroup work on different experts. Used when that fits a few tens of KB.
-// This form also multiplies in FP16, which halves the dequantisation work (the
+// Staged forms (kXAll, kXExpert): the workgroup copies activation rows into LDS and
+// the waves read their MFMA operand from there. This frees the 16 registers per stage
+// that the fragment otherwise takes, so more weight tiles are in flight. kXAll copies
+// all of `act` (the batch's tokens for up, all routed rows for down) once, which lets
+// the waves of a workgroup work on different experts; kXExpert copies, per pass, the
+// rows of the one expert whose consecutive block pairs the workgroup takes.
+// The staged forms also multiply in FP16, which halves the dequantisation work (the
 // kernel is close to bound by it): the staged rows are scaled by a power of two each
 // (max |x| below 2^15) and converted to FP16, the weights are exact in FP16 (see
 // dequant8_f16), and the FP32 outputs are scaled back. Scaling by a power of two
 // scales every FP32 partial sum exactly, so the result has the same bits as the BF16
 // form as long as a row's values lie within 2^32 of its maximum (smaller ones round
 // to FP16 subnormals, a change below 2^-40 of the row's largest term).
-template <bool kUp, int D, bool kXLds>
+template <bool kUp, int D, int kX>
 __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
+  constexpr bool kLds = kX != kXRegs;
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_npass;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -174,13 +188,16 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   const int gi = wave / ksplit, q = wave % ksplit;
   const int K = a.K, NS = K / 128, NB = a.N / 16;
   const int pairs_per_group = kUp ? a.I / 16 : a.N / 32;
-  // this wave group's unit: spread over dispatch slots (see Placement)
+  // this wave group's unit: spread over dispatch slots, or the workgroup's `groups`
+  // consecutive pairs (of one expert: pairs_per_group is a multiple of 4)
   const int b = blockIdx.x, C = a.slots;
-  const int unit = ((b / C) * groups + gi) * C + (b % C);
+  const int unit = kX == kXExpert ? b * groups + gi : ((b / C) * groups + gi) * C + (b % C);
   const Group grp = find_group(a, unit / pairs_per_group);
   const int g = grp.g, r0 = grp.r0, M = grp.M;
   const int pair = unit % pairs_per_group;
-  const int npass = (M + 15) / 16;
+  // rows per pass: an MFMA's 16, or the staged rows of the expert form
+  const int rows_pass = kX == kXExpert ? a.stage_rows : 16;
+  const int npass = (M + rows_pass - 1) / rows_pass;
 
   // the pair's two blocks (row-block indices within the expert)
   int b0, b1, col0;
@@ -206,17 +223,17 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   const int nsl = kSlices / ksplit, first = q * nsl;
   const int s_begin = first * NS / kSlices, s_end = (first + nsl) * NS / kSlices;
   const int xs = x_row_stride(K);
-  // slices of waves q > 0 handed to wave 0: [groups][kSlices - nsl][2][64] float4,
-  // after the staged activations when those are in LDS
-  float4* red = reinterpret_cast<float4*>(smem + (kXLds ? x_stage_bytes(a.stage_rows, K) : 0));
-  float* row_scale = reinterpret_cast<float*>(smem + (size_t)a.stage_rows * xs);  // LDS form
+  // LDS: staged rows, their FP32 scales, then the slices of waves q > 0 handed to
+  // wave 0 ([groups][kSlices - nsl][2][64] float4)
+  float4* red = reinterpret_cast<float4*>(smem + (kLds ? x_stage_bytes(a.stage_rows, K) : 0));
+  float* row_scale = reinterpret_cast<float*>(smem + (size_t)a.stage_rows * xs);
 
-  Stage<kXLds> st[D];
+  Stage<kX> st[D];
   const uint16_t* arow = nullptr;
   // steps past the wave's range re-read its last step; a wave with an empty range
   // (NS < kSlices) reads step 0 and never uses it: every wave issues the same loads,
   // so the wait counts after them do not depend on the path taken
-  auto issue = [&](Stage<kXLds>& t, int s) {
+  auto issue = [&](Stage<kX>& t, int s) {
     s = s < s_end ? s : s_end - 1;
     s = s > 0 ? s : 0;
     const int co = s * 1024 + lane * 16, so = s * 128 + lane * 2;
@@ -224,46 +241,34 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
     t.c1 = load_b128_nt(rc1, co);
     t.s0 = load_b16(rs0, so);
     t.s1 = load_b16(rs1, so);
-    if constexpr (!kXLds) {
+    if constexpr (!kLds) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) t.x[j] = *reinterpret_cast<const u32x4*>(arow + s * 128 + 8 * j);
     }
   };
-  // this lane's activation row in pass `pass`: its token (up: the routed pair's
-  // index, divided by k by row_src) or its routed row (down); rows past the pass's
-  // real rows use the pass's first row (MFMA rows are independent and those rows are
-  // not stored)
+  // the activation row of pass row rn (rows past the pass's real rows use the pass's
+  // first row: MFMA rows are independent and those rows are not stored): the routed
+  // pair's index for up (row_src divides it by k) or the routed row for down
   auto row_pair = [&](int pass) {
-    const int nr = min(16, M - pass * 16);
-    const int r = r0 + pass * 16 + (rn < nr ? rn : 0);
+    const int nr = min(rows_pass, M - pass * rows_pass);
+    const int r = r0 + pass * rows_pass + (rn < nr ? rn : 0);
     return kUp && a.perm_src ? a.perm_src[r] : r;
   };
   auto row_src = [&](int pair_or_row) { return kUp && a.perm_src ? pair_or_row / a.k : pair_or_row; };
-  // LDS form: pass 0's row index, then its first tiles go out before the
-  // workgroup-wide activation copy below, so the three round trips overlap (the
-  // index is only used, and so only waited for, after the copy)
-  int src = 0, pair0 = 0;
-  if (kXLds && npass > 0) {
-    pair0 = row_pair(0);
-#pragma unroll
-    for (int i = 0; i < D - 1; ++i) issue(st[i], s_begin + i);
-  }
 
-  // passes of the workgroup: the most of its groups (the K-split hand-over below is
-  // a workgroup barrier, so every wave runs the same number of passes)
-  if (tid == 0) s_npass = 0;
-  __syncthreads();
-  if (lane == 0 && q == 0 && npass > 0) atomicMax(&s_npass, npass);
-  if constexpr (kXLds) {
-    // all rows of act -> LDS rows of x_row_stride(K) bytes
+  // copy rows [row0, row0 + nrows) of LDS from act rows srcrow(i), then convert them
+  // in place to FP16, each scaled by 2^-sh so that its max |x| is below 2^15, keeping
+  // 2^sh in row_scale (the caller synchronises before and after)
+  auto stage_rows = [&](int nrows, auto srcrow) {
     const int cpr = K / 8;  // 16-byte chunks per row
-    const int total = a.stage_rows * cpr;
+    const int total = nrows * cpr;
     auto copy8 = [&](int base) {  // 8 chunks per thread: all loads, then all stores
       u32x4 buf[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int c = base + u * 256 + tid;
-        buf[u] = reinterpret_cast<const u32x4*>(a.act)[c < total ? c : 0];
+        const int cc = c < total ? c : 0;
+        buf[u] = reinterpret_cast<const u32x4*>(a.act + (size_t)srcrow(cc / cpr) * K)[cc % cpr];
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -272,13 +277,11 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
       }
     };
     // the first round outside the loop: a loop head would wait for every load in
-    // flight (the tiles above included) before reusing its registers
+    // flight (the weight tiles issued before included) before reusing its registers
     copy8(0);
     for (int base = 8 * 256; base < total; base += 8 * 256) copy8(base);
     __syncthreads();
-    // BF16 -> FP16 in place, row by row (wave w takes rows w, w+4, ...): scale each row
-    // by 2^-sh so that its max |x| is below 2^15, and keep 2^sh for the outputs
-    for (int row = wave; row < a.stage_rows; row += 4) {
+    for (int row = wave; row < nrows; row += 4) {  // wave w converts rows w, w+4, ...
       uint8_t* rp = smem + (size_t)row * xs;
       float mx = 0.f;
       for (int c = lane; c < cpr; c += 64) {
@@ -301,37 +304,64 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
       }
       if (lane == 0) row_scale[row] = __builtin_ldexpf(1.0f, sh);
     }
+  };
+
+  // Staged forms: pass 0's row index, then its first tiles go out before the
+  // activation copy, so the round trips overlap (the index is waited for only where
+  // it is used, after the copy's loads have been issued)
+  int src = 0, pair0 = 0;
+  if (kLds && npass > 0) {
+    pair0 = row_pair(0);
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) issue(st[i], s_begin + i);
+  }
+  // passes of the workgroup: the most of its groups (the K-split hand-over and the
+  // expert form's copies are workgroup barriers, so every wave runs as many passes)
+  if (tid == 0) s_npass = 0;
+  __syncthreads();
+  if (lane == 0 && q == 0 && npass > 0) atomicMax(&s_npass, npass);
+  if constexpr (kX == kXAll) {
+    stage_rows(a.stage_rows, [&](int i) { return i; });
+    __syncthreads();
   }
   __syncthreads();
   const int npass_wg = s_npass;
   if (npass_wg == 0) return;  // workgroup-uniform
-  if (kXLds) src = row_src(pair0);
   const float ts = M > 0 ? a.tscale[g] : 0.f;
 
   for (int pass = 0; pass < npass_wg; ++pass) {
     const bool active = pass < npass;  // wave-group-uniform
-    const int nr = active ? min(16, M - pass * 16) : 0;  // real rows in this pass
+    const int nr = active ? min(rows_pass, M - pass * rows_pass) : 0;  // real rows in this pass
+    if constexpr (kX == kXExpert) {
+      // the expert's rows of this pass (one expert per workgroup: all waves agree)
+      if (pass > 0) {
+        __syncthreads();  // the previous pass's reads are done
+        pair0 = row_pair(pass);
+      }
+      stage_rows(nr, [&](int i) { return row_src(__shfl(pair0, i)); });
+      __syncthreads();
+    }
     f32x4 tot0 = {0.f, 0.f, 0.f, 0.f}, tot1 = tot0;
     if (active) {
-      if (!kXLds || pass > 0) {  // the LDS form primed pass 0 before the activation copy
+      if constexpr (kX == kXAll) {
+        if (pass == 0) src = row_src(pair0);
+      }
+      if (!kLds || pass > 0) {  // the staged forms primed pass 0 before their copy
         src = row_src(row_pair(pass));
         arow = a.act + (size_t)src * K + kq * 32;
 #pragma unroll
         for (int i = 0; i < D - 1; ++i) issue(st[i], s_begin + i);
       }
-      const uint8_t* xl = smem + (size_t)src * xs + kq * 64;
+      // LDS row: the staged token/row (all rows) or the pass row (expert rows)
+      const int lrow = kX == kXExpert ? (rn < nr ? rn : 0) : src;
+      const uint8_t* xl = smem + (size_t)lrow * xs + kq * 64;
       // acc: the running slice; tot: slices first..current, summed in order (wave q = 0)
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-      auto compute = [&](const Stage<kXLds>& t, int s) {
+      auto compute = [&](const Stage<kX>& t, int s) {
         u32x4 xv[4];
-        if constexpr (kXLds) {
+        if constexpr (kLds) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const u32x4*>(xl + s * 256 + 16 * j);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) xv[j] = t.x[j];
-        }
-        if constexpr (kXLds) {
           const f16x2 sa = e4m3x2_to_f16(t.s0), sb = e4m3x2_to_f16(t.s1);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -339,6 +369,8 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
             acc1 = mfma16x16x32_f16(xv[j], dequant8_f16(t.c1[j], j < 2 ? sb[0] : sb[1]), acc1);
           }
         } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xv[j] = t.x[j];
           const float sa0 = e4m3_to_f32<0>(t.s0), sa1 = e4m3_to_f32<1>(t.s0);
           const float sb0 = e4m3_to_f32<0>(t.s1), sb1 = e4m3_to_f32<1>(t.s1);
 #pragma unroll
@@ -393,10 +425,12 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
     }
     if (active && q == 0) {
       const int mbase = 4 * kq;  // pass rows mbase..mbase+3, column rn
-      if constexpr (kXLds) {  // undo the rows' FP16 scaling (exact: powers of two)
+      if constexpr (kLds) {  // undo the rows' FP16 scaling (exact: powers of two)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float sc = row_scale[__shfl(src, mbase + i)];  // lane mbase+i reads row mbase+i
+          // lane mbase+i holds pass row mbase+i's staged row (all-rows form)
+          const int srow = __shfl(src, mbase + i);
+          const float sc = row_scale[kX == kXExpert ? (mbase + i < nr ? mbase + i : 0) : srow];
           tot0[i] *= sc;
           tot1[i] *= sc;
         }
@@ -404,7 +438,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (mbase + i < nr) {
-          const size_t row = (size_t)(r0 + pass * 16 + mbase + i);
+          const size_t row = (size_t)(r0 + pass * rows_pass + mbase + i);
           if (kUp) {
             a.out[row * a.I + col0 + rn] = f32_to_bf16(silu_mul(ts * tot0[i], ts * tot1[i]));
           } else {
@@ -437,24 +471,36 @@ int cu_count() {
   return cached;
 }
 
-// rows: routed rows R (T*k, or T when dense); stage_rows: rows of `act`
-hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int G, int stage_rows,
-                  hipStream_t s) {
+// all_rows: rows of `act` (T for up, the routed rows for down); expert_rows: the most
+// rows one expert can have in a decode batch (T: a token routes to an expert once)
+hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int G, long long all_rows,
+                  long long expert_rows, hipStream_t s) {
   DecodeArgs a = base;
   a.G = G;
   // when fewer experts can have rows than exist, units only for as many as can
   a.compact = active_groups < G;
   const long long pairs_per_group = up ? a.I / 16 : a.N / 32;
   const long long pairs = active_groups * pairs_per_group;
-  const size_t x_bytes = x_stage_bytes(stage_rows, a.K);
-  const bool use_lds = x_bytes <= kXLdsMaxBytes;
-  a.stage_rows = use_lds ? stage_rows : 0;
+  // the activation source: all rows in LDS if they fit, else each expert's rows
+  // (at most 16 per pass), else registers
+  const int rows_alloc = (int)std::min<long long>(expert_rows, 16);
+  int mode = kXRegs;
+  int stage_rows = 0;
+  if (x_stage_bytes((int)std::min<long long>(all_rows, 1 << 20), a.K) <= kXLdsMaxBytes) {
+    mode = kXAll;
+    stage_rows = (int)all_rows;
+  } else if (x_stage_bytes(rows_alloc, a.K) <= kXLdsMaxBytes) {
+    mode = kXExpert;
+    stage_rows = rows_alloc;
+  }
+  a.stage_rows = stage_rows;
+  const size_t x_bytes = mode == kXRegs ? 0 : x_stage_bytes(stage_rows, a.K);
   // K split: the most waves per pair for which the whole grid is resident at once,
   // so that every wave starts in the first wave of dispatch and no second, partial
   // round of waves trails behind (a wave's lifetime is a few memory latencies)
   auto lds_bytes = [&](int ks) {
     const size_t red = ks > 1 ? (size_t)(4 / ks) * (kSlices - kSlices / ks) * 2 * 64 * 16 : 0;
-    return (use_lds ? x_bytes : 0) + red;
+    return x_bytes + red;
   };
   const int cus = cu_count();
   auto resident_waves = [&](int ks) {
@@ -476,18 +522,23 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
   // a whole number of rounds of `slots` workgroups, so that unit <-> (workgroup,
   // group) is one to one. The spread placement is for grids that are resident at
   // once; larger ones keep consecutive units (the same expert's pairs, whose rows
-  // the workgroup's waves share in cache) together (slots = 1).
+  // the workgroup's waves share in cache) together (slots = 1). The expert form
+  // always takes consecutive units.
   const bool one_round = pairs * ks <= resident_waves(ks);
-  const long long slots = one_round ? std::min<long long>(wgs, cus) : 1;
+  const long long slots = one_round && mode != kXExpert ? std::min<long long>(wgs, cus) : 1;
   a.slots = (int)slots;
   const long long grid = (wgs + slots - 1) / slots * slots;
   const unsigned lds = (unsigned)lds_bytes(ks);
-  if (use_lds) {
-    if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesLds, true>), dim3((unsigned)grid), dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesLds, true>), dim3((unsigned)grid), dim3(256), lds, s, a);
+  const dim3 g3((unsigned)grid), b3(256);
+  if (mode == kXAll) {
+    if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesLds, kXAll>), g3, b3, lds, s, a);
+    else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesLds, kXAll>), g3, b3, lds, s, a);
+  } else if (mode == kXExpert) {
+    if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesLds, kXExpert>), g3, b3, lds, s, a);
+    else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesLds, kXExpert>), g3, b3, lds, s, a);
   } else {
-    if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesReg, false>), dim3((unsigned)grid), dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesReg, false>), dim3((unsigned)grid), dim3(256), lds, s, a);
+    if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesReg, kXRegs>), g3, b3, lds, s, a);
+    else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesReg, kXRegs>), g3, b3, lds, s, a);
   }
   return hipGetLastError();
 }
@@ -499,7 +550,7 @@ hipError_t launch_ffn_up_decode(const uint16_t* x, const int32_t* offsets, const
   if (T == 0) return hipSuccess;
   DecodeArgs a{x, offsets, perm_src, k, T, w13.packed, w13.scales, w13.tscale, 2 * I, H, I, 1, h, G, 0, 1, 0};
   const long long active = offsets ? std::min<long long>((long long)T * k, G) : 1;
-  return launch(true, a, active, offsets ? G : 1, T, s);
+  return launch(true, a, active, offsets ? G : 1, T, T, s);
 }
 
 hipError_t launch_ffn_down_decode(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H, int I,
@@ -508,8 +559,7 @@ hipError_t launch_ffn_down_decode(const uint16_t* h, const int32_t* offsets, int
   DecodeArgs a{h, offsets, nullptr, 1, T, w2.packed, w2.scales, w2.tscale, H, I, I, 1, y, G, 0, 1, 0};
   const long long rows = offsets ? (long long)T * k : T;
   const long long active = offsets ? std::min<long long>((long long)T * k, G) : 1;
-  const int stage_rows = rows <= (1 << 20) ? (int)rows : (1 << 20);
-  return launch(false, a, active, offsets ? G : 1, stage_rows, s);
+  return launch(false, a, active, offsets ? G : 1, rows, T, s);
 }
 
 }  // namespace moe4

@@ -222,7 +222,10 @@ FFN_CASES = [
     ("decode_t1", None, None),
     ("decode_t8", None, None),
     ("batched_t64", None, None),
-    # many rows per expert: several passes of the small-row kernel, ragged tails
+    # rows of one expert staged per pass (all rows do not fit LDS), several passes,
+    # K split over the workgroup's waves
+    ("expert_staged", wl.Workload("expert_staged", T=40, H=512, E=4, k=2, I=1024, routing="zipf"), None),
+    # many rows per expert (the MFMA-tile kernel), ragged tails
     ("rows_ragged", wl.Workload("rows_ragged", T=301, H=512, E=8, k=2, I=256, routing="zipf"), None),
     ("prefill_small", wl.Workload("prefill_small", T=1024, H=1024, E=16, k=4, I=384, routing="zipf"), None),
 ]

@@ -225,6 +225,10 @@ FFN_CASES = [
     # rows of one expert staged per pass (all rows do not fit LDS), several passes,
     # K split over the workgroup's waves
     ("expert_staged", wl.Workload("expert_staged", T=40, H=512, E=4, k=2, I=1024, routing="zipf"), None),
+    # all rows staged once, many experts with rows
+    ("all_staged", wl.Workload("all_staged", T=8, H=1024, E=256, k=8, I=1536, routing="normal"), None),
+    # activations in registers (neither all rows nor one expert's rows fit LDS), several passes
+    ("regs_passes", wl.Workload("regs_passes", T=40, H=2048, E=4, k=2, I=256, routing="zipf"), None),
     # many rows per expert (the MFMA-tile kernel), ragged tails
     ("rows_ragged", wl.Workload("rows_ragged", T=301, H=512, E=8, k=2, I=256, routing="zipf"), None),
     ("prefill_small", wl.Workload("prefill_small", T=1024, H=1024, E=16, k=4, I=384, routing="zipf"), None),
@@ -439,6 +443,49 @@ def test_layer_deterministic_and_batch_independent():
     assert np.array_equal(c["idx"][0], a["idx"][3])
     assert np.array_equal(c["o_bits"][0], a["o_bits"][3])
     assert np.array_equal(c["n_bits"][0], a["n_bits"][3])
+
+
+# moe4_layer takes the fused top-k + plan launch for small batches and may pick other
+# kernel forms than the separate entry points; both must give the same bytes. The
+# cases span one to 136 routed pairs.
+FUSED_ROUTE_CASES = [
+    ("tiny", None), ("decode_t1", None), ("decode_t8", None),
+    ("pairs_128", wl.Workload("pairs_128", T=16, H=256, E=64, k=8, I=256, routing="normal")),
+    ("pairs_136", wl.Workload("pairs_136", T=17, H=256, E=64, k=8, I=256, routing="normal")),
+]
+
+
+@pytest.mark.parametrize("name,w", FUSED_ROUTE_CASES, ids=[c[0] for c in FUSED_ROUTE_CASES])
+def test_layer_matches_entry_points(name, w):
+    w = wl.workload(name) if w is None else w
+    note(f"layer vs entry points: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
+    inp = wl.make_inputs(w, seed=2)
+    g = GpuLayer(inp)
+    g.run()
+    a = g.host()
+    T, k, E, H, I = inp.T, w.k, w.E, w.H, w.I
+    shape = g.shape
+    logits = g.logits.clone() if inp.logits is not None else torch.empty((T, E), dtype=torch.float32,
+                                                                           device="cuda")
+    idx = torch.full((T, k), -1, dtype=torch.int32, device="cuda")
+    tw = torch.zeros((T, k), dtype=torch.float32, device="cuda")
+    B.moe4_route(shape, g.x if g.w_router is not None else None, g.w_router, logits, idx, tw)
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    n = B.moe4_permute_workspace_bytes(shape)
+    B.moe4_permute(shape, idx, off, perm, inv, torch.empty(n, dtype=torch.uint8, device="cuda") if n else None)
+    h = torch.zeros((T * k, I), dtype=torch.int16, device="cuda")
+    y = torch.zeros((T * k, H), dtype=torch.int16, device="cuda")
+    B.moe4_expert_ffn(shape, g.x, off, perm, g.w13, g.w2, h, y)
+    o = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    nrm = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    B.moe4_combine_norm(shape, y, inv, tw, None, g.residual, g.gamma, o, nrm)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), a["idx"])
+    assert np.array_equal(tw.cpu().numpy().view(np.int32), g.topk_w.cpu().numpy().view(np.int32))
+    assert np.array_equal(to_host_bits(o), a["o_bits"])
+    assert np.array_equal(to_host_bits(nrm), a["n_bits"])
 
 
 def test_layer_t0_is_a_noop():

@@ -8,21 +8,25 @@
 // compute"). So the 4-bit weights are dequantised exactly into BF16 once per
 // workgroup tile and fed to BF16 MFMAs with FP32 accumulation.
 //
-// Tiling. A workgroup (4 waves) computes a 256-row x 256-column output tile of one
-// expert over K in steps of 64; each wave owns 128 x 128 of it as 4 x 4 blocks of
-// 32x32x16 MFMAs (on gfx950 this shape runs near the BF16 peak, while 16x16x32 tops
-// out near half of it). For the up projection the 256 weight rows are 128 gate rows and
-// the matching 128 up rows, so each wave holds gate and up accumulators of the same
-// h columns in the same lanes and applies SwiGLU in registers.
+// Tiling. A workgroup (8 waves, two per SIMD) computes a 256-row x 256-column output
+// tile of one expert over K in steps of 64; each wave owns 128 x 64 of it as 4 x 2
+// blocks of 32x32x16 MFMAs (on gfx950 this shape runs near the BF16 peak, while
+// 16x16x32 tops out near half of it). Two waves per SIMD let one wave's MFMAs run while
+// the other waits on LDS or does its share of the dequantisation (with one wave of
+// 128 x 128 per SIMD the same tile ran slower). For the up projection the 256 weight
+// rows are 128 gate rows and the matching 128 up rows, and each wave takes 32 of each,
+// so gate and up accumulators of the same h columns sit in the same lanes and SwiGLU
+// is applied in registers. An expert's last tile, when it has at most 128 rows, is
+// computed by the four waves of rows 0..127 alone; the other four only help fill LDS.
 //
 // Pipeline. Activation rows (gathered through perm_src for the up projection) and
 // weight half-tiles (tiled layout, 512 contiguous bytes per 16-row block) are loaded
-// into registers two K steps ahead; during step i's MFMAs, step i+1's registers are
+// into registers ahead of use; during step i's MFMAs, step i+1's registers are
 // dequantised (code * E4M3 scale is exact in BF16) and written to the other LDS
 // buffer part by part, each part's registers then refilled with step i+2. One
 // barrier per step. Each 16-wide K substep reads its operand fragments from LDS while
-// the previous one's MFMAs run. LDS rows are XOR-swizzled
-// in 16-byte chunks so the MFMA operand reads spread over the banks.
+// the previous one's MFMAs run. LDS rows are XOR-swizzled in 16-byte chunks so the
+// MFMA operand reads spread over the banks.
 //
 // Scheduling. One grid covers (expert M-tile, N-tile) pairs up to a bound; each
 // workgroup finds its expert by scanning the per-expert tile counts from the
@@ -37,7 +41,7 @@ namespace moe4 {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kXcds = 8;
 
 struct GemmArgs {
@@ -120,25 +124,25 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   const float ts = a.tscale[g];
 
   // ---- global -> register loads ----
-  // A: thread t loads rows t/8 + 32i (i = 0..7), 16-byte chunk t%8 of the step. Rows
+  // A: thread t loads rows t/8 + 64i (i = 0..3), 16-byte chunk t%8 of the step. Rows
   // past the tile's end read the tile's first row instead: their results are never
   // stored, so they need no masking.
   const int a_chunk = tid & 7;
-  const uint16_t* a_src[8];
+  const uint16_t* a_src[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rr = (tid >> 3) + 32 * i;
+  for (int i = 0; i < 4; ++i) {
+    const int rr = (tid >> 3) + 64 * i;
     int src = row0 + (rr < rows ? rr : 0);
     if (kUp && a.perm_src) src = a.perm_src[src] / a.k;
     a_src[i] = a.act + (size_t)src * K + a_chunk * 8;
   }
-  // B: units u = tid, tid + 256: 16-row block u/32, lane-in-half-tile u%32
-  const uint8_t* b_code[2];
-  const uint8_t* b_scale[2];
-  int b_st[2];  // LDS element offset of the unit's row (its 4 chunks are 4*kq' + j)
+  // B: unit u = tid: 16-row block u/32, lane-in-half-tile u%32
+  const uint8_t* b_code[1];
+  const uint8_t* b_scale[1];
+  int b_st[1];  // LDS element offset of the unit's row (its 4 chunks are 4*kq' + j)
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int u = tid + 256 * h;
+  for (int h = 0; h < 1; ++h) {
+    const int u = tid;
     const int blk = u >> 5, l = u & 31;
     int wblk;  // weight row-block of this LDS block
     if (kUp) wblk = blk < 8 ? (nt * 128) / 16 + blk : (a.I + nt * 128) / 16 + (blk - 8);
@@ -153,65 +157,57 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   // row a lane touches, (r >> 1) & 7 depends only on the lane, so the addresses are a
   // per-lane base plus immediate offsets.
   const int a_sw = ((tid >> 3) >> 1) & 7;
-  const int a_st = (tid >> 3) * BK + ((a_chunk ^ a_sw) << 3);  // + 32*i*BK for row group i
+  const int a_st = (tid >> 3) * BK + ((a_chunk ^ a_sw) << 3);  // + 64*i*BK for row group i
   const int b_sw = ((tid & 15) >> 1) & 7;
 
-  u32x4 ra[8], rb[2];
-  uint32_t rs[2];
-  // Part q of step st's global loads: activation rows 2q, 2q+1 of this thread and, for
-  // odd q, weight unit q/2 (whose two store parts have then both been written).
+  u32x4 ra[4], rb[1];
+  uint32_t rs[1];
+  // Part q of step st's global loads: activation row q of this thread and, for q = 3,
+  // the weight unit (whose four store parts have then all been written).
   auto load_part = [&](int st, int q) {
     const int k0 = st * BK;
-#pragma unroll
-    for (int i = 2 * q; i < 2 * q + 2; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + k0);
-    if (q & 1) {
-      const int h = q >> 1;
+    ra[q] = *reinterpret_cast<const u32x4*>(a_src[q] + k0);
+    if (q == 3) {
+      const int h = 0;
       const size_t toff = (size_t)(st >> 1) * 1024 + (st & 1) * 512;
       const size_t soff = (size_t)(st >> 1) * 128 + (st & 1) * 64;
       rb[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b_code[h] + toff));
       rs[h] = *reinterpret_cast<const uint16_t*>(b_scale[h] + soff);
     }
   };
-  // Part q (0..3) of writing the loaded step into LDS buffer `buf`: activation rows
-  // 2q and 2q+1 of this thread, and two of the eight BF16 chunks of weight unit q/2
-  // (dequantised here).
+  // Part q (0..3) of writing the loaded step into LDS buffer `buf`: activation row q
+  // of this thread, and BF16 chunk q of the weight unit (dequantised here).
   auto store_part = [&](int buf, int q) {
-#pragma unroll
-    for (int i = 2 * q; i < 2 * q + 2; ++i)
-      *reinterpret_cast<u32x4*>(&lds_a[buf][a_st + 32 * i * BK]) = ra[i];
-    const int h = q >> 1;
-    const float sc = (q & 1) ? e4m3_to_f32<1>(rs[h]) : e4m3_to_f32<0>(rs[h]);
-#pragma unroll
-    for (int j = 2 * (q & 1); j < 2 * (q & 1) + 2; ++j)
-      *reinterpret_cast<u32x4*>(&lds_b[buf][b_st[h] * BK + (((4 * b_kq + j) ^ b_sw) << 3)]) =
-          dequant8(rb[h][j], sc);
+    *reinterpret_cast<u32x4*>(&lds_a[buf][a_st + 64 * q * BK]) = ra[q];
+    const float sc = q < 2 ? e4m3_to_f32<0>(rs[0]) : e4m3_to_f32<1>(rs[0]);
+    *reinterpret_cast<u32x4*>(&lds_b[buf][b_st[0] * BK + (((4 * b_kq + q) ^ b_sw) << 3)]) = dequant8(rb[0][q], sc);
   };
 
-  // ---- per-wave tile: 128 rows x 128 LDS B rows as 4 x 4 blocks of 32x32x16 MFMAs ----
-  const int wm = wave >> 1, wn = wave & 1;
+  // ---- per-wave tile: 128 rows x 64 LDS B rows as 4 x 2 blocks of 32x32x16 MFMAs ----
+  const int wm = wave >> 2, wn = wave & 3;
   const int r32 = lane & 31, kh = lane >> 5;  // operand row within a 32-block; K half (8 values)
   // LDS B rows of block j: up = gate rows 64wn + 32j (j < 2) then up rows
   // 128 + 64wn + 32(j-2); down = rows 128wn + 32j. Row offsets are multiples of 32.
-  int boff[4];
+  int boff[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) boff[j] = kUp ? (j < 2 ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2)) : 128 * wn + 32 * j;
+  for (int j = 0; j < 2; ++j) boff[j] = kUp ? 128 * j + 32 * wn : 64 * wn + 32 * j;
   const int f_sw = (r32 >> 1) & 7;
   const int fa_base = (128 * wm + r32) * BK, fb_base = r32 * BK;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // operand fragments of one 16-wide K substep
-  u32x4 fa[4], fb[4], na[4], nb[4];
+  u32x4 fa[4], fb[2], na[4], nb[2];
   auto read_frags = [&](int buf, int ks, u32x4* A, u32x4* Bv) {
     const int cs = ((2 * ks + kh) ^ f_sw) << 3;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Bv[j] = *reinterpret_cast<const u32x4*>(&lds_b[buf][fb_base + boff[j] * BK + cs]);
+    for (int j = 0; j < 2; ++j) Bv[j] = *reinterpret_cast<const u32x4*>(&lds_b[buf][fb_base + boff[j] * BK + cs]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const u32x4*>(&lds_a[buf][fa_base + 32 * i * BK + cs]);
   };
@@ -224,6 +220,20 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) load_part(min(1, nsteps - 1), q);
   __syncthreads();
+  // A tile of at most 128 rows (an expert's last, partial tile) leaves the waves of the
+  // lower half (wm = 1) without rows: they only copy their share of every step into LDS.
+  if (rows <= 128 && wm == 1) {
+    for (int st = 0; st < nsteps; ++st) {
+      const int next2 = min(st + 2, nsteps - 1);
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        store_part((st & 1) ^ 1, ks);
+        load_part(next2, ks);
+      }
+      __syncthreads();
+    }
+    return;
+  }
   read_frags(0, 0, fa, fb);
   for (int st = 0; st < nsteps; ++st) {
     const int buf = st & 1;
@@ -238,15 +248,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
       store_part(buf ^ 1, ks);
       load_part(next2, ks);
       if (ks + 1 < BK / 16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          fa[i] = na[i];
-          fb[i] = nb[i];
-        }
+        for (int i = 0; i < 4; ++i) fa[i] = na[i];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[j] = nb[j];
       }
     }
     __syncthreads();
@@ -262,15 +271,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
       if (tr < rows) {
         const size_t orow = (size_t)(row0 + tr);
         if (kUp) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = nt * 128 + 64 * wn + 32 * j + r32;
-            a.out[orow * a.I + col] = f32_to_bf16(silu_mul(ts * acc[i][j][r], ts * acc[i][j + 2][r]));
+          {
+            const int col = nt * 128 + 32 * wn + r32;
+            a.out[orow * a.I + col] = f32_to_bf16(silu_mul(ts * acc[i][0][r], ts * acc[i][1][r]));
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = nt * BN + 128 * wn + 32 * j + r32;
+          for (int j = 0; j < 2; ++j) {
+            const int col = nt * BN + 64 * wn + 32 * j + r32;
             a.out[orow * a.N + col] = f32_to_bf16(ts * acc[i][j][r]);
           }
         }

@@ -446,12 +446,15 @@ def test_layer_deterministic_and_batch_independent():
 
 
 # moe4_layer takes the fused top-k + plan launch for small batches and may pick other
-# kernel forms than the separate entry points; both must give the same bytes. The
-# cases span one to 136 routed pairs.
+# kernel forms than the separate entry points; both must give the same bytes, on every
+# one of several calls. The cases span one to 136 routed pairs, given or computed
+# router logits, and one or two token groups of the router.
 FUSED_ROUTE_CASES = [
     ("tiny", None), ("decode_t1", None), ("decode_t8", None),
     ("pairs_128", wl.Workload("pairs_128", T=16, H=256, E=64, k=8, I=256, routing="normal")),
     ("pairs_136", wl.Workload("pairs_136", T=17, H=256, E=64, k=8, I=256, routing="normal")),
+    ("router_t16", wl.Workload("router_t16", T=16, H=256, E=64, k=8, I=256, routing="router")),
+    ("router_t17", wl.Workload("router_t17", T=17, H=256, E=64, k=8, I=256, routing="router")),
 ]
 
 
@@ -463,6 +466,11 @@ def test_layer_matches_entry_points(name, w):
     g = GpuLayer(inp)
     g.run()
     a = g.host()
+    for _ in range(2):
+        g.run()
+        b = g.host()
+        assert np.array_equal(b["idx"], a["idx"]) and np.array_equal(b["o_bits"], a["o_bits"])
+        assert np.array_equal(b["n_bits"], a["n_bits"])
     T, k, E, H, I = inp.T, w.k, w.E, w.H, w.I
     shape = g.shape
     logits = g.logits.clone() if inp.logits is not None else torch.empty((T, E), dtype=torch.float32,

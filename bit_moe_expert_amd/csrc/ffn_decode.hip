@@ -59,6 +59,7 @@ enum XMode {
   kXRegs = 0,    // global memory, loaded into registers with each K step
   kXAll = 1,     // LDS: all rows of `act`, staged once per workgroup
   kXExpert = 2,  // LDS: the rows of the workgroup's expert, staged per pass
+  kXSlice = 3,   // LDS: the rows of the workgroup's expert, staged per pass and K slice
 };
 
 // One K step of a wave: its two 16 x 128 weight tiles and, when the activations are
@@ -76,6 +77,11 @@ struct Stage<kXAll> {
 };
 template <>
 struct Stage<kXExpert> {
+  u32x4 c0, c1;
+  uint32_t s0, s1;
+};
+template <>
+struct Stage<kXSlice> {
   u32x4 c0, c1;
   uint32_t s0, s1;
 };
@@ -176,9 +182,14 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 // scales every FP32 partial sum exactly, so the result has the same bits as the BF16
 // form as long as a row's values lie within 2^32 of its maximum (smaller ones round
 // to FP16 subnormals, a change below 2^-40 of the row's largest term).
+// kXSlice stages the expert's rows one fixed K slice at a time (for rows too long to
+// stage whole), each (row, slice) with its own power of two; a slice's partial sums are
+// scaled back before they are added, which keeps the same bits for the same reason.
 template <bool kUp, int D, int kX>
 __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   constexpr bool kLds = kX != kXRegs;
+  constexpr bool kSlice = kX == kXSlice;
+  constexpr bool kPerExpert = kX == kXExpert || kSlice;  // workgroup = one expert's pairs
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_npass;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -191,12 +202,12 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   // this wave group's unit: spread over dispatch slots, or the workgroup's `groups`
   // consecutive pairs (of one expert: pairs_per_group is a multiple of 4)
   const int b = blockIdx.x, C = a.slots;
-  const int unit = kX == kXExpert ? b * groups + gi : ((b / C) * groups + gi) * C + (b % C);
+  const int unit = kPerExpert ? b * groups + gi : ((b / C) * groups + gi) * C + (b % C);
   const Group grp = find_group(a, unit / pairs_per_group);
   const int g = grp.g, r0 = grp.r0, M = grp.M;
   const int pair = unit % pairs_per_group;
   // rows per pass: an MFMA's 16, or the staged rows of the expert form
-  const int rows_pass = kX == kXExpert ? a.stage_rows : 16;
+  const int rows_pass = kPerExpert ? a.stage_rows : 16;
   const int npass = (M + rows_pass - 1) / rows_pass;
 
   // the pair's two blocks (row-block indices within the expert)
@@ -222,7 +233,8 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   // depend on ksplit, i.e. on how many tokens share the call.
   const int nsl = kSlices / ksplit, first = q * nsl;
   const int s_begin = first * NS / kSlices, s_end = (first + nsl) * NS / kSlices;
-  const int xs = x_row_stride(K);
+  const int NSL = NS / kSlices;  // K steps per slice (kXSlice: a multiple of D)
+  const int xs = x_row_stride(kSlice ? K / kSlices : K);
   // LDS: staged rows, their FP32 scales, then the slices of waves q > 0 handed to
   // wave 0 ([groups][kSlices - nsl][2][64] float4)
   float4* red = reinterpret_cast<float4*>(smem + (kLds ? x_stage_bytes(a.stage_rows, K) : 0));
@@ -256,22 +268,25 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   };
   auto row_src = [&](int pair_or_row) { return kUp && a.perm_src ? pair_or_row / a.k : pair_or_row; };
 
-  // copy rows [row0, row0 + nrows) of LDS from act rows srcrow(i), then convert them
-  // in place to FP16, each scaled by 2^-sh so that its max |x| is below 2^15, keeping
-  // 2^sh in row_scale (the caller synchronises before and after)
-  auto stage_rows = [&](int nrows, auto srcrow) {
-    const int cpr = K / 8;  // 16-byte chunks per row
+  // copy columns [k0, k0 + kc) of act rows srcrow(i), i < nrows, into LDS rows i, then
+  // convert them in place to FP16, each scaled by 2^-sh so that its max |x| is below
+  // 2^15, keeping 2^sh in row_scale (the caller synchronises before and after)
+  auto stage_rows = [&](int nrows, auto srcrow, int k0, int kc) {
+    const int cpr = kc / 8;  // 16-byte chunks per row
     const int total = nrows * cpr;
-    auto copy8 = [&](int base) {  // 8 chunks per thread: all loads, then all stores
-      u32x4 buf[8];
+    // kU chunks per thread: all loads, then all stores (fewer in the slice form, whose
+    // copies run while the K loop's registers are live)
+    constexpr int kU = kSlice ? 2 : 8;
+    auto copy8 = [&](int base) {
+      u32x4 buf[kU];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const int c = base + u * 256 + tid;
         const int cc = c < total ? c : 0;
-        buf[u] = reinterpret_cast<const u32x4*>(a.act + (size_t)srcrow(cc / cpr) * K)[cc % cpr];
+        buf[u] = reinterpret_cast<const u32x4*>(a.act + (size_t)srcrow(cc / cpr) * K + k0)[cc % cpr];
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const int c = base + u * 256 + tid;
         if (c < total) *reinterpret_cast<u32x4*>(smem + (size_t)(c / cpr) * xs + (c % cpr) * 16) = buf[u];
       }
@@ -279,7 +294,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
     // the first round outside the loop: a loop head would wait for every load in
     // flight (the weight tiles issued before included) before reusing its registers
     copy8(0);
-    for (int base = 8 * 256; base < total; base += 8 * 256) copy8(base);
+    for (int base = kU * 256; base < total; base += kU * 256) copy8(base);
     __syncthreads();
     for (int row = wave; row < nrows; row += 4) {  // wave w converts rows w, w+4, ...
       uint8_t* rp = smem + (size_t)row * xs;
@@ -321,7 +336,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   __syncthreads();
   if (lane == 0 && q == 0 && npass > 0) atomicMax(&s_npass, npass);
   if constexpr (kX == kXAll) {
-    stage_rows(a.stage_rows, [&](int i) { return i; });
+    stage_rows(a.stage_rows, [&](int i) { return i; }, 0, K);
     __syncthreads();
   }
   __syncthreads();
@@ -338,8 +353,20 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
         __syncthreads();  // the previous pass's reads are done
         pair0 = row_pair(pass);
       }
-      stage_rows(nr, [&](int i) { return row_src(__shfl(pair0, i)); });
+      stage_rows(nr, [&](int i) { return row_src(__shfl(pair0, i)); }, 0, K);
       __syncthreads();
+    }
+    // the expert's rows of this pass, K slice `slc` (the caller synchronises before)
+    auto stage_slice = [&](int slc) {
+      stage_rows(nr, [&](int i) { return row_src(__shfl(pair0, i)); }, slc * (K / kSlices), K / kSlices);
+      __syncthreads();
+    };
+    if constexpr (kSlice) {
+      if (pass > 0) {
+        __syncthreads();  // the previous pass's reads are done
+        pair0 = row_pair(pass);
+      }
+      stage_slice(0);
     }
     f32x4 tot0 = {0.f, 0.f, 0.f, 0.f}, tot1 = tot0;
     if (active) {
@@ -353,7 +380,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
         for (int i = 0; i < D - 1; ++i) issue(st[i], s_begin + i);
       }
       // LDS row: the staged token/row (all rows) or the pass row (expert rows)
-      const int lrow = kX == kXExpert ? (rn < nr ? rn : 0) : src;
+      const int lrow = kPerExpert ? (rn < nr ? rn : 0) : src;
       const uint8_t* xl = smem + (size_t)lrow * xs + kq * 64;
       // acc: the running slice; tot: slices first..current, summed in order (wave q = 0)
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
@@ -361,7 +388,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
         u32x4 xv[4];
         if constexpr (kLds) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const u32x4*>(xl + s * 256 + 16 * j);
+          for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const u32x4*>(xl + (kSlice ? s % NSL : s) * 256 + 16 * j);
           const f16x2 sa = e4m3x2_to_f16(t.s0), sb = e4m3x2_to_f16(t.s1);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -382,7 +409,14 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
       };
       // close slice `sl`: wave 0 adds it to its running total; other waves hand it over
       auto close_slice = [&](int sl) {
-        if (q == 0) {
+        if constexpr (kSlice) {  // scale the slice back first (exact: powers of two)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float sc = row_scale[4 * kq + i < nr ? 4 * kq + i : 0];
+            tot0[i] += acc0[i] * sc;
+            tot1[i] += acc1[i] * sc;
+          }
+        } else if (q == 0) {
           tot0 += acc0;
           tot1 += acc1;
         } else {
@@ -397,6 +431,12 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
       if (s_begin < s_end) {
         while (sl < first + nsl && (sl + 1) * NS / kSlices <= s_begin) close_slice(sl++);  // empty slices
         for (int sb = s_begin; sb < s_end; sb += D) {
+          if constexpr (kSlice) {
+            if (sb > s_begin && sb % NSL == 0) {  // the next slice's rows
+              __syncthreads();  // every wave is done with the previous slice
+              stage_slice(sb / NSL);
+            }
+          }
 #pragma unroll
           for (int i = 0; i < D; ++i) {
             issue(st[(i + D - 1) % D], sb + i + D - 1);
@@ -425,7 +465,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
     }
     if (active && q == 0) {
       const int mbase = 4 * kq;  // pass rows mbase..mbase+3, column rn
-      if constexpr (kLds) {  // undo the rows' FP16 scaling (exact: powers of two)
+      if constexpr (kLds && !kSlice) {  // undo the rows' FP16 scaling (exact: powers of two)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // lane mbase+i holds pass row mbase+i's staged row (all-rows form)
@@ -492,9 +532,13 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
   } else if (x_stage_bytes(rows_alloc, a.K) <= kXLdsMaxBytes) {
     mode = kXExpert;
     stage_rows = rows_alloc;
+  } else if (a.K % (kSlices * 128 * kStagesLds) == 0 && x_stage_bytes(rows_alloc, a.K / kSlices) <= kXLdsMaxBytes) {
+    mode = kXSlice;  // a slice's steps are whole rounds of the ring
+    stage_rows = rows_alloc;
   }
   a.stage_rows = stage_rows;
-  const size_t x_bytes = mode == kXRegs ? 0 : x_stage_bytes(stage_rows, a.K);
+  const size_t x_bytes =
+      mode == kXRegs ? 0 : x_stage_bytes(stage_rows, mode == kXSlice ? a.K / kSlices : a.K);
   // K split: the most waves per pair for which the whole grid is resident at once,
   // so that every wave starts in the first wave of dispatch and no second, partial
   // round of waves trails behind (a wave's lifetime is a few memory latencies)
@@ -511,6 +555,7 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
   };
   int ks = 1;
   for (int cand : {4, 2}) {
+    if (mode == kXSlice) break;  // the workgroup's waves go through the slices together
     if (pairs * cand <= resident_waves(cand)) {
       ks = cand;
       break;
@@ -525,7 +570,7 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
   // the workgroup's waves share in cache) together (slots = 1). The expert form
   // always takes consecutive units.
   const bool one_round = pairs * ks <= resident_waves(ks);
-  const long long slots = one_round && mode != kXExpert ? std::min<long long>(wgs, cus) : 1;
+  const long long slots = one_round && mode != kXExpert && mode != kXSlice ? std::min<long long>(wgs, cus) : 1;
   a.slots = (int)slots;
   const long long grid = (wgs + slots - 1) / slots * slots;
   const unsigned lds = (unsigned)lds_bytes(ks);
@@ -536,6 +581,9 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
   } else if (mode == kXExpert) {
     if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesLds, kXExpert>), g3, b3, lds, s, a);
     else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesLds, kXExpert>), g3, b3, lds, s, a);
+  } else if (mode == kXSlice) {
+    if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesLds, kXSlice>), g3, b3, lds, s, a);
+    else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesLds, kXSlice>), g3, b3, lds, s, a);
   } else {
     if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesReg, kXRegs>), g3, b3, lds, s, a);
     else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesReg, kXRegs>), g3, b3, lds, s, a);

@@ -274,9 +274,8 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   auto stage_rows = [&](int nrows, auto srcrow, int k0, int kc) {
     const int cpr = kc / 8;  // 16-byte chunks per row
     const int total = nrows * cpr;
-    // kU chunks per thread: all loads, then all stores (fewer in the slice form, whose
-    // copies run while the K loop's registers are live)
-    constexpr int kU = kSlice ? 2 : 8;
+    // 8 chunks per thread: all loads, then all stores
+    constexpr int kU = 8;
     auto copy8 = [&](int base) {
       u32x4 buf[kU];
 #pragma unroll
@@ -291,10 +290,24 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
         if (c < total) *reinterpret_cast<u32x4*>(smem + (size_t)(c / cpr) * xs + (c % cpr) * 16) = buf[u];
       }
     };
-    // the first round outside the loop: a loop head would wait for every load in
-    // flight (the weight tiles issued before included) before reusing its registers
-    copy8(0);
-    for (int base = kU * 256; base < total; base += kU * 256) copy8(base);
+    if constexpr (kSlice) {
+      // straight into LDS, every load of the slice in flight at once: a wave moves 1 KB
+      // blocks (lane l's 16 bytes land at block + 16 l), a row's slice being kc / 512
+      // of them
+      const int bpr = kc / 512;
+      for (int bi = wave; bi < nrows * bpr; bi += 4) {
+        const int r = bi / bpr, h = bi % bpr;
+        const uint16_t* src = a.act + (size_t)srcrow(r) * K + k0 + h * 512 + lane * 8;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(smem + (size_t)r * xs + h * 1024),
+                                         16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      // the first round outside the loop: a loop head would wait for every load in
+      // flight (the weight tiles issued before included) before reusing its registers
+      copy8(0);
+      for (int base = kU * 256; base < total; base += kU * 256) copy8(base);
+    }
     __syncthreads();
     for (int row = wave; row < nrows; row += 4) {  // wave w converts rows w, w+4, ...
       uint8_t* rp = smem + (size_t)row * xs;

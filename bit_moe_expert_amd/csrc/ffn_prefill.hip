@@ -21,10 +21,12 @@
 //
 // Pipeline. Activation rows (gathered through perm_src for the up projection) and
 // weight half-tiles (tiled layout, 512 contiguous bytes per 16-row block) are loaded
-// into registers ahead of use; during step i's MFMAs, step i+1's registers are
-// dequantised (code * E4M3 scale is exact in BF16) and written to the other LDS
-// buffer part by part, each part's registers then refilled with step i+2. One
-// barrier per step. Each 16-wide K substep reads its operand fragments from LDS while
+// into one of two register sets two steps ahead of use; during step i's MFMAs, step
+// i+1's set is dequantised (code * E4M3 scale is exact in BF16) and written to the
+// other LDS buffer part by part, each part's registers then refilled with step i+3.
+// The weights are read through the caches: every M-tile of an expert reads the same
+// weight tiles, and the tile order keeps those workgroups on one XCD. One barrier
+// per step. Each 16-wide K substep reads its operand fragments from LDS while
 // the previous one's MFMAs run. LDS rows are XOR-swizzled in 16-byte chunks so the
 // MFMA operand reads spread over the banks.
 //
@@ -33,6 +35,8 @@
 // offsets. Workgroup ids are remapped so each XCD (ids are dealt round-robin to the
 // 8 XCDs) gets a contiguous run of tiles with N fastest: the workgroups sharing an
 // activation tile, and an expert's weights, meet in the same L2.
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -160,28 +164,34 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   const int a_st = (tid >> 3) * BK + ((a_chunk ^ a_sw) << 3);  // + 64*i*BK for row group i
   const int b_sw = ((tid & 15) >> 1) & 7;
 
-  u32x4 ra[4], rb[1];
-  uint32_t rs[1];
-  // Part q of step st's global loads: activation row q of this thread and, for q = 3,
-  // the weight unit (whose four store parts have then all been written).
-  auto load_part = [&](int st, int q) {
+  // Two register sets, used by alternate steps: step s's data is loaded during step
+  // s - 2 and written to LDS during step s - 1, so every load has a whole step and more
+  // to arrive.
+  u32x4 ra[2][4], rb[2];
+  uint32_t rs[2];
+  // Part q of step st's global loads into set S: activation row q of this thread and,
+  // for q = 3, the weight unit (whose four store parts have then all been written).
+  auto load_part = [&](auto SET, int st, int q) {
+    constexpr int S = decltype(SET)::value;
     const int k0 = st * BK;
-    ra[q] = *reinterpret_cast<const u32x4*>(a_src[q] + k0);
+    ra[S][q] = *reinterpret_cast<const u32x4*>(a_src[q] + k0);
     if (q == 3) {
-      const int h = 0;
       const size_t toff = (size_t)(st >> 1) * 1024 + (st & 1) * 512;
       const size_t soff = (size_t)(st >> 1) * 128 + (st & 1) * 64;
-      rb[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b_code[h] + toff));
-      rs[h] = *reinterpret_cast<const uint16_t*>(b_scale[h] + soff);
+      rb[S] = *reinterpret_cast<const u32x4*>(b_code[0] + toff);
+      rs[S] = *reinterpret_cast<const uint16_t*>(b_scale[0] + soff);
     }
   };
-  // Part q (0..3) of writing the loaded step into LDS buffer `buf`: activation row q
-  // of this thread, and BF16 chunk q of the weight unit (dequantised here).
-  auto store_part = [&](int buf, int q) {
-    *reinterpret_cast<u32x4*>(&lds_a[buf][a_st + 64 * q * BK]) = ra[q];
-    const float sc = q < 2 ? e4m3_to_f32<0>(rs[0]) : e4m3_to_f32<1>(rs[0]);
-    *reinterpret_cast<u32x4*>(&lds_b[buf][b_st[0] * BK + (((4 * b_kq + q) ^ b_sw) << 3)]) = dequant8(rb[0][q], sc);
+  // Part q (0..3) of writing set S into LDS buffer `buf`: activation row q of this
+  // thread, and BF16 chunk q of the weight unit (dequantised here).
+  auto store_part = [&](auto SET, int buf, int q) {
+    constexpr int S = decltype(SET)::value;
+    *reinterpret_cast<u32x4*>(&lds_a[buf][a_st + 64 * q * BK]) = ra[S][q];
+    const float sc = q < 2 ? e4m3_to_f32<0>(rs[S]) : e4m3_to_f32<1>(rs[S]);
+    *reinterpret_cast<u32x4*>(&lds_b[buf][b_st[0] * BK + (((4 * b_kq + q) ^ b_sw) << 3)]) = dequant8(rb[S][q], sc);
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
 
   // ---- per-wave tile: 128 rows x 64 LDS B rows as 4 x 2 blocks of 32x32x16 MFMAs ----
   const int wm = wave >> 2, wn = wave & 3;
@@ -212,36 +222,41 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
     for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const u32x4*>(&lds_a[buf][fa_base + 32 * i * BK + cs]);
   };
 
-  // Prologue: step 0 into LDS buffer 0, step 1 into the registers.
+  // Prologue: step 0 into LDS buffer 0, steps 1 and 2 into register sets 1 and 0.
 #pragma unroll
-  for (int q = 0; q < 4; ++q) load_part(0, q);
+  for (int q = 0; q < 4; ++q) load_part(S0{}, 0, q);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) store_part(0, q);
+  for (int q = 0; q < 4; ++q) store_part(S0{}, 0, q);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) load_part(min(1, nsteps - 1), q);
+  for (int q = 0; q < 4; ++q) load_part(S1{}, min(1, nsteps - 1), q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) load_part(S0{}, min(2, nsteps - 1), q);
   __syncthreads();
   // A tile of at most 128 rows (an expert's last, partial tile) leaves the waves of the
   // lower half (wm = 1) without rows: they only copy their share of every step into LDS.
+  // Steps come in pairs (K is a multiple of 128): step st writes set (st + 1) % 2.
   if (rows <= 128 && wm == 1) {
-    for (int st = 0; st < nsteps; ++st) {
-      const int next2 = min(st + 2, nsteps - 1);
+    auto copy_step = [&](auto SET, int st) {
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
-        store_part((st & 1) ^ 1, ks);
-        load_part(next2, ks);
+        store_part(SET, (st & 1) ^ 1, ks);
+        load_part(SET, min(st + 3, nsteps - 1), ks);
       }
       __syncthreads();
+    };
+    for (int st = 0; st < nsteps; st += 2) {
+      copy_step(S1{}, st);
+      copy_step(S0{}, st + 1);
     }
     return;
   }
   read_frags(0, 0, fa, fb);
-  for (int st = 0; st < nsteps; ++st) {
+  auto step = [&](auto SET, int st) {
     const int buf = st & 1;
-    const int next2 = min(st + 2, nsteps - 1);  // the last steps reload themselves (never read)
+    const int next3 = min(st + 3, nsteps - 1);  // the last steps reload themselves (never read)
     // Four 16-wide substeps. In each, the next substep's fragments are read while this
-    // one's MFMAs run; then one part of step st+1 (loaded during step st-1) is written
-    // to the other buffer, and its registers are refilled with step st+2, which thus
-    // has a whole step to arrive.
+    // one's MFMAs run; then one part of step st+1 is written to the other buffer, and
+    // its registers are refilled with step st+3.
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       if (ks + 1 < BK / 16) read_frags(buf, ks + 1, na, nb);
@@ -249,8 +264,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
-      store_part(buf ^ 1, ks);
-      load_part(next2, ks);
+      store_part(SET, buf ^ 1, ks);
+      load_part(SET, next3, ks);
       if (ks + 1 < BK / 16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) fa[i] = na[i];
@@ -260,6 +275,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
     }
     __syncthreads();
     read_frags(buf ^ 1, 0, fa, fb);
+  };
+  for (int st = 0; st < nsteps; st += 2) {
+    step(S1{}, st);
+    step(S0{}, st + 1);
   }
 
   // ---- epilogue: acc[i][j][r] is row 8(r/4) + 4kh + r%4, column r32 of block (i, j) ----

@@ -242,12 +242,9 @@ def _plan_on_host(inp):
     return idx, w, off, perm, inv
 
 
-@pytest.mark.parametrize("name,w,_", FFN_CASES, ids=[c[0] for c in FFN_CASES])
-def test_expert_ffn_routed(name, w, _):
-    w = wl.workload(name) if w is None else w
-    note(f"expert ffn routed: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
-    inp = wl.make_inputs(w, seed=1)
-    idx, _, off, perm, inv = _plan_on_host(inp)
+def _check_routed_ffn(inp, w, off, perm):
+    """Runs moe4_expert_ffn on the plan (off, perm) and checks h against the oracle's
+    SwiGLU and y against the oracle's down projection of the GPU's own h."""
     shape = B.make_shape(inp.T, w.H, w.E, w.k, w.I)
     w13, w2, *_ = upload_weights(inp)
     R = inp.T * w.k
@@ -270,6 +267,29 @@ def test_expert_ffn_routed(name, w, _):
         ref_y[rows] = oracle.bf16_round(got_h[rows] @ W2.T)
     assert_bf16_close(got_h, ref_h, "h")
     assert_bf16_close(got_y, ref_y, "y", slack_rms=2.0 ** -16)
+
+
+@pytest.mark.parametrize("name,w,_", FFN_CASES, ids=[c[0] for c in FFN_CASES])
+def test_expert_ffn_routed(name, w, _):
+    w = wl.workload(name) if w is None else w
+    note(f"expert ffn routed: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
+    inp = wl.make_inputs(w, seed=1)
+    idx, _, off, perm, inv = _plan_on_host(inp)
+    _check_routed_ffn(inp, w, off, perm)
+
+
+def test_expert_ffn_tile_edges():
+    """Expert groups on the prefill GEMM's tile boundaries: 128 rows (a half-height
+    tile), 129 (a full tile with one row in its lower half), 256, 257, 384 (a full tile
+    and a half one) and 1 row."""
+    counts = [128, 129, 256, 257, 384, 1]
+    w = wl.Workload("tile_edges", T=sum(counts), H=512, E=len(counts), k=1, I=256, routing="normal")
+    note(f"expert ffn tile edges: groups {counts}")
+    inp = wl.make_inputs(w, seed=3)
+    idx = np.random.default_rng(5).permutation(np.repeat(np.arange(w.E), counts)).astype(np.int32)[:, None]
+    off, perm, inv = oracle.permute(idx, w.E)
+    assert np.array_equal(np.diff(off), counts)
+    _check_routed_ffn(inp, w, off, perm)
 
 
 def test_expert_ffn_dense_shared():

@@ -516,6 +516,50 @@ def test_layer_matches_entry_points(name, w):
     assert np.array_equal(to_host_bits(nrm), a["n_bits"])
 
 
+GRAPH_CASES = [
+    ("decode_t8", None),
+    ("prefill_small", wl.Workload("prefill_small", T=1024, H=1024, E=16, k=4, I=384, routing="zipf")),
+]
+
+
+@pytest.mark.parametrize("name,w", GRAPH_CASES, ids=[c[0] for c in GRAPH_CASES])
+def test_layer_graph_replay(name, w):
+    """moe4_layer captured into a HIP graph (torch.cuda.CUDAGraph) and replayed several
+    times, with eager calls and synchronisations in between: every replay must give
+    the eager call's bytes."""
+    w = wl.workload(name) if w is None else w
+    note(f"layer graph replay: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
+    inp = wl.make_inputs(w, seed=4)
+    if w.routing == "router":
+        condition_router_margin(inp)
+    g = GpuLayer(inp)
+    g.run()
+    ref = g.host()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.run()  # warm-up on the capture stream's side
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.run()
+    for _ in range(3):
+        g.res_out.zero_()
+        g.norm_out.zero_()
+        g.topk_idx.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = g.host()
+        assert np.array_equal(got["idx"], ref["idx"])
+        assert np.array_equal(got["o_bits"], ref["o_bits"]) and np.array_equal(got["n_bits"], ref["n_bits"])
+        g.run()  # eager work between the replays
+        torch.cuda.synchronize()
+        again = g.host()
+        assert np.array_equal(again["o_bits"], ref["o_bits"])
+
+
 def test_layer_t0_is_a_noop():
     w = wl.workload("tiny")
     inp = wl.make_inputs(w, seed=0, T=0)

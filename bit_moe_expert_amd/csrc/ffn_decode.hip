@@ -16,15 +16,17 @@
 // streams them along K. When the routing leaves too few blocks to fill the chip
 // (ksplit > 1), the K range of a pair is split over ksplit waves of the workgroup,
 // and their partial sums are added in a fixed order through LDS. Each K step is
-// dequantised exactly into BF16 (code * E4M3 scale has at most 6 significant bits)
-// in registers while the next steps' tiles are in flight.
+// dequantised exactly (code * E4M3 scale has at most 6 significant bits) in registers
+// while the next steps' tiles are in flight: into BF16 when the activations come from
+// registers, into FP16 when they are staged in LDS (see the staged forms below).
 //
 // Placement. When the grid is resident at once, the (expert, block pair) units are
 // dealt to workgroups with a stride of one round of workgroups (unit = round * C +
 // slot, C = min(workgroups, CUs)), so the units of each dispatch slot, and hence of
 // each CU, differ by at most one whatever the routing; larger grids give each
-// workgroup consecutive units (C = 1). When T*k < E only as many experts as can have rows are laid out and
-// each wave finds its expert among the non-empty ones from the offsets.
+// workgroup consecutive units (C = 1). When T*k < E only as many experts as can have
+// rows are laid out, and each wave finds its expert among the non-empty ones from the
+// offsets.
 #include <algorithm>
 
 #include "device.hpp"

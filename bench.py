@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--side-stream", choices=["on", "off"], default="off",
+                    help="routed chain on a side stream beside the shared expert (moe4_layer_side)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB twice with torch (a plain copy of known size, for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -179,11 +181,16 @@ def main():
     norm_out = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
     ws = torch.empty(B.moe4_layer_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
 
+    use_side = args.side_stream == "on" and w.n_shared > 0
+    side = torch.cuda.Stream() if use_side else None
+    if use_side:
+        log("routed chain on a side stream, shared expert on the launch stream")
+
     def layer_step(i):
         c = per_chunk[i % chunks]
         a13, a2 = weights[(i // chunks) % copies]
         B.moe4_layer(shape, c["x"], wr, c["logits"], a13, a2, s13, s2, c["residual"], gamma, topk_idx,
-                     topk_w, res_out, norm_out, ws)
+                     topk_w, res_out, norm_out, ws, side_stream=side)
 
     stream = torch.cuda.current_stream()
     if args.copy_calibration:
@@ -283,7 +290,7 @@ def main():
                        f"E={w.E}{'+%d shared' % w.n_shared if w.n_shared else ''} top-{w.k} I={w.I}, "
                        f"W4A16 (E2M1 + E4M3/16 + FP32)",
            "T": T * chunks, "H": w.H, "E": w.E, "k": w.k, "I": w.I, "n_shared": w.n_shared,
-           "weight_copies_rotated": copies, "routing": w.routing}
+           "weight_copies_rotated": copies, "routing": w.routing, "side_stream": use_side}
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

@@ -52,6 +52,9 @@ SIGNATURES = {
     "moe4_layer": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, _W4, _W4, _W4, _W4, c_void_p,
                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                            c_void_p]),
+    "moe4_layer_side": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, _W4, _W4, _W4, _W4, c_void_p,
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                c_void_p, c_void_p, c_void_p, c_void_p]),
 }
 
 ABI_VERSION = 1

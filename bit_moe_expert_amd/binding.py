@@ -152,12 +152,16 @@ def moe4_combine_norm(shape: Shape, y, inv, topk_w, shared_y, residual, gamma, r
 
 def moe4_layer(shape: Shape, x, w_router, logits, w13: DeviceW4, w2: DeviceW4,
                shared13: Optional[DeviceW4], shared2: Optional[DeviceW4], residual, gamma,
-               topk_idx, topk_w, residual_out, normed_out, ws, stream=None) -> None:
+               topk_idx, topk_w, residual_out, normed_out, ws, stream=None, side_stream=None,
+               events=None) -> None:
+    """The whole layer. With ``side_stream`` (a torch.cuda.Stream) the routed chain runs
+    there while ``stream`` runs the shared expert (moe4_layer_side); ``events`` is a pair
+    of torch.cuda.Event for the fork and the join (created on first use if omitted)."""
     T, H, E, k = shape.T, shape.H, shape.E, shape.k
     d13, d2 = w13.desc(), w2.desc()
     s13 = shared13.desc() if shared13 is not None else None
     s2 = shared2.desc() if shared2 is not None else None
-    check(_lib.load().moe4_layer(
+    args = (
         shape, _ptr(x, "x", _BF16_LIKE, T * H), _ptr(w_router, "w_router", _BF16_LIKE, E * H),
         _ptr(logits, "logits", (torch.float32,), T * E), d13, d2, s13, s2,
         _ptr(residual, "residual", _BF16_LIKE, T * H), _ptr(gamma, "gamma", _BF16_LIKE, H),
@@ -165,4 +169,24 @@ def moe4_layer(shape: Shape, x, w_router, logits, w13: DeviceW4, w2: DeviceW4,
         _ptr(topk_w, "topk_w", (torch.float32,), T * k),
         _ptr(residual_out, "residual_out", _BF16_LIKE, T * H),
         _ptr(normed_out, "normed_out", _BF16_LIKE, T * H),
-        _ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    if side_stream is None:
+        check(_lib.load().moe4_layer(*args))
+        return
+    fork, join = events if events is not None else side_events()
+    check(_lib.load().moe4_layer_side(*args, side_stream.cuda_stream, fork.cuda_event, join.cuda_event))
+
+
+_SIDE_EVENTS = {}
+
+
+def side_events():
+    """Two events of the current device for moe4_layer's fork and join, created once
+    (recorded once here so that they exist; make the first call outside graph capture)."""
+    dev = torch.cuda.current_device()
+    if dev not in _SIDE_EVENTS:
+        evs = (torch.cuda.Event(), torch.cuda.Event())
+        for ev in evs:
+            ev.record()
+        _SIDE_EVENTS[dev] = evs
+    return _SIDE_EVENTS[dev]

@@ -294,12 +294,13 @@ moe4_status moe4_combine_norm(const moe4_shape* shape, const uint16_t* y, const 
   return MOE4_OK;
 }
 
-moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
+static moe4_status layer_impl(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
                        float* logits, const moe4_w4* w13, const moe4_w4* w2,
                        const moe4_w4* shared13, const moe4_w4* shared2,
                        const uint16_t* residual, const uint16_t* gamma, int32_t* topk_idx,
                        float* topk_w, uint16_t* residual_out, uint16_t* normed_out, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       size_t ws_bytes, void* stream, void* side_stream, void* fork_event,
+                       void* join_event) {
   g_err[0] = 0;
   moe4_status st = check_shape(shape);
   if (st) return st;
@@ -319,6 +320,9 @@ moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_
   NEED(topk_w, "topk_w");
   NEED(residual_out, "residual_out");
   NEED(normed_out, "normed_out");
+  const bool two_streams = shape->n_shared && side_stream && side_stream != stream;
+  if (two_streams && (!fork_event || !join_event))
+    return fail(MOE4_ERR_INVALID_ARG, "a side stream needs fork_event and join_event");
   const LayerWs L = layer_ws_layout(shape);
   if (ws == nullptr || ws_bytes < L.total)
     return fail(MOE4_ERR_WORKSPACE, "layer needs %zu workspace bytes, got %zu%s", L.total, ws_bytes,
@@ -333,10 +337,19 @@ moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_
   uint16_t* h = reinterpret_cast<uint16_t*>(base + L.h);
   uint16_t* y = reinterpret_cast<uint16_t*>(base + L.y);
   const size_t pairs = (size_t)shape->T * shape->k;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t main = static_cast<hipStream_t>(stream);
+  // the routed chain runs on the side stream when there is one (the shared expert
+  // stays on the main stream, which then waits for the chain before the combine)
+  hipStream_t s = two_streams ? static_cast<hipStream_t>(side_stream) : main;
   const int T = shape->T, H = shape->H, E = shape->E, k = shape->k, I = shape->I;
 
   hipError_t e;
+  if (two_streams) {
+    e = hipEventRecord(static_cast<hipEvent_t>(fork_event), main);
+    if (e != hipSuccess) return hip_fail(e, "fork event record");
+    e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(fork_event), 0);
+    if (e != hipSuccess) return hip_fail(e, "side stream wait");
+  }
   if (w_router) {
     e = moe4::launch_router_logits(x, w_router, logits, T, H, E, s);
     if (e != hipSuccess) return hip_fail(e, "router_logits launch");
@@ -358,16 +371,43 @@ moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_
   if (shape->n_shared) {
     uint16_t* hs = h + pairs * I;
     uint16_t* ys = y + pairs * H;
-    e = moe4::launch_ffn_up(x, nullptr, nullptr, k, T, 1, H, I, view(shared13), hs, s);
+    e = moe4::launch_ffn_up(x, nullptr, nullptr, k, T, 1, H, I, view(shared13), hs, main);
     if (e != hipSuccess) return hip_fail(e, "shared ffn up launch");
-    e = moe4::launch_ffn_down(hs, nullptr, k, T, 1, H, I, view(shared2), ys, s);
+    e = moe4::launch_ffn_down(hs, nullptr, k, T, 1, H, I, view(shared2), ys, main);
     if (e != hipSuccess) return hip_fail(e, "shared ffn down launch");
     shared_y = ys;
   }
+  if (two_streams) {
+    e = hipEventRecord(static_cast<hipEvent_t>(join_event), s);
+    if (e != hipSuccess) return hip_fail(e, "join event record");
+    e = hipStreamWaitEvent(main, static_cast<hipEvent_t>(join_event), 0);
+    if (e != hipSuccess) return hip_fail(e, "main stream wait");
+  }
   e = moe4::launch_combine_norm(y, inv, topk_w, shared_y, residual, gamma, residual_out, normed_out, T,
-                                H, k, shape->eps, s);
+                                H, k, shape->eps, main);
   if (e != hipSuccess) return hip_fail(e, "combine_norm launch");
   return MOE4_OK;
+}
+
+moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                       float* logits, const moe4_w4* w13, const moe4_w4* w2,
+                       const moe4_w4* shared13, const moe4_w4* shared2,
+                       const uint16_t* residual, const uint16_t* gamma, int32_t* topk_idx,
+                       float* topk_w, uint16_t* residual_out, uint16_t* normed_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return layer_impl(shape, x, w_router, logits, w13, w2, shared13, shared2, residual, gamma, topk_idx, topk_w,
+                    residual_out, normed_out, ws, ws_bytes, stream, nullptr, nullptr, nullptr);
+}
+
+moe4_status moe4_layer_side(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                            float* logits, const moe4_w4* w13, const moe4_w4* w2,
+                            const moe4_w4* shared13, const moe4_w4* shared2,
+                            const uint16_t* residual, const uint16_t* gamma, int32_t* topk_idx,
+                            float* topk_w, uint16_t* residual_out, uint16_t* normed_out, void* ws,
+                            size_t ws_bytes, void* stream, void* side_stream, void* fork_event,
+                            void* join_event) {
+  return layer_impl(shape, x, w_router, logits, w13, w2, shared13, shared2, residual, gamma, topk_idx, topk_w,
+                    residual_out, normed_out, ws, ws_bytes, stream, side_stream, fork_event, join_event);
 }
 
 }  // extern "C"

@@ -200,6 +200,27 @@ moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_
                        float* topk_w, uint16_t* residual_out, uint16_t* normed_out, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* The whole layer with the routed chain on a side stream (#627, jschmied's comment of
+ * Oct 14 on where one step's time goes: the router, top-k, plan and routed experts run
+ * on a side stream while the main stream runs the shared expert and then waits for
+ * them). Arguments as for moe4_layer, plus:
+ *   side_stream  a hipStream_t (as void*) for the router, plan and routed experts.
+ *   fork_event, join_event  two hipEvent_t (as void*) owned by the caller: fork_event
+ *                is recorded on `stream` and waited for by side_stream before the
+ *                chain; join_event is recorded on side_stream after it and waited for
+ *                by `stream` before the combine, which runs on `stream`.
+ * With n_shared == 0, or side_stream NULL or equal to `stream`, this is moe4_layer
+ * (the events are not used). Results are bit-identical to moe4_layer. Missing events
+ * with a distinct side stream and a shared expert are MOE4_ERR_INVALID_ARG. The events
+ * and streams make the call capturable into a HIP graph as a fork and join. */
+moe4_status moe4_layer_side(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                            float* logits, const moe4_w4* w13, const moe4_w4* w2,
+                            const moe4_w4* shared13, const moe4_w4* shared2,
+                            const uint16_t* residual, const uint16_t* gamma, int32_t* topk_idx,
+                            float* topk_w, uint16_t* residual_out, uint16_t* normed_out, void* ws,
+                            size_t ws_bytes, void* stream, void* side_stream, void* fork_event,
+                            void* join_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,10 +76,11 @@ class GpuLayer:
         self.ws = torch.empty(max(1, B.moe4_layer_workspace_bytes(self.shape)), dtype=torch.uint8,
                               device="cuda")
 
-    def run(self, stream=None):
+    def run(self, stream=None, side_stream=None):
         B.moe4_layer(self.shape, self.x, self.w_router, self.logits, self.w13, self.w2,
                      self.shared13, self.shared2, self.residual, self.gamma, self.topk_idx,
-                     self.topk_w, self.res_out, self.norm_out, self.ws, stream=stream)
+                     self.topk_w, self.res_out, self.norm_out, self.ws, stream=stream,
+                     side_stream=side_stream)
 
     def host(self):
         torch.cuda.synchronize()

@@ -123,6 +123,23 @@ def test_layer_workspace_and_shared_checks():
     assert st == _lib.MOE4_ERR_INVALID_ARG and b"shared13" in lib.moe4_last_error()
 
 
+def test_layer_side_needs_events():
+    """A distinct side stream with a shared expert needs both events; the check comes
+    before anything is enqueued (the stream handles are never used)."""
+    lib = _lib.load()
+    sh = shape(n_shared=1)
+    w = W4(FAKE, FAKE, FAKE)
+    side = ctypes.c_void_p(0x2000)
+    st = lib.moe4_layer_side(sh, FAKE, None, FAKE, w, w, w, w, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, 1 << 40, None, side, None, FAKE)
+    assert st == _lib.MOE4_ERR_INVALID_ARG and b"fork_event" in lib.moe4_last_error()
+    # without a shared expert the side stream is not used, and the other checks still apply
+    s = shape()
+    st = lib.moe4_layer_side(s, FAKE, None, FAKE, w, w, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, 16, None, side, None, None)
+    assert st == _lib.MOE4_ERR_WORKSPACE
+
+
 def test_prepack_checks():
     lib = _lib.load()
     assert lib.moe4_prepack_w4(1, 48, 256, FAKE, FAKE, FAKE, FAKE, None) == _lib.MOE4_ERR_UNSUPPORTED

@@ -560,6 +560,45 @@ def test_layer_graph_replay(name, w):
         assert np.array_equal(again["o_bits"], ref["o_bits"])
 
 
+SIDE_CASES = [
+    ("shared_decode", wl.Workload("shared_decode", T=8, H=1024, E=32, k=4, I=256, routing="normal",
+                                  n_shared=1)),
+    ("shared_prefill", wl.Workload("shared_prefill", T=1024, H=1024, E=8, k=2, I=256, routing="zipf",
+                                   n_shared=1)),
+]
+
+
+@pytest.mark.parametrize("name,w", SIDE_CASES, ids=[c[0] for c in SIDE_CASES])
+def test_layer_side_stream(name, w):
+    """moe4_layer_side (routed chain on a side stream, shared expert on the main stream)
+    gives moe4_layer's bytes, eagerly and captured into a HIP graph as a fork and join."""
+    note(f"layer side stream: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} shared={w.n_shared}")
+    inp = wl.make_inputs(w, seed=5)
+    g = GpuLayer(inp)
+    g.run()
+    ref = g.host()
+    side = torch.cuda.Stream()
+    for _ in range(2):
+        g.res_out.zero_()
+        g.norm_out.zero_()
+        torch.cuda.synchronize()
+        g.run(side_stream=side)
+        got = g.host()
+        assert np.array_equal(got["idx"], ref["idx"])
+        assert np.array_equal(got["o_bits"], ref["o_bits"]) and np.array_equal(got["n_bits"], ref["n_bits"])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.run(side_stream=side)
+    for _ in range(2):
+        g.res_out.zero_()
+        g.norm_out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = g.host()
+        assert np.array_equal(got["o_bits"], ref["o_bits"]) and np.array_equal(got["n_bits"], ref["n_bits"])
+
+
 def test_layer_t0_is_a_noop():
     w = wl.workload("tiny")
     inp = wl.make_inputs(w, seed=0, T=0)

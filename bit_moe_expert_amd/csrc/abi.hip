@@ -294,13 +294,13 @@ moe4_status moe4_combine_norm(const moe4_shape* shape, const uint16_t* y, const 
   return MOE4_OK;
 }
 
+// The layer on `stream`, or with the routed chain on `side_stream` (see moe4_layer_side).
 static moe4_status layer_impl(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
-                       float* logits, const moe4_w4* w13, const moe4_w4* w2,
-                       const moe4_w4* shared13, const moe4_w4* shared2,
-                       const uint16_t* residual, const uint16_t* gamma, int32_t* topk_idx,
-                       float* topk_w, uint16_t* residual_out, uint16_t* normed_out, void* ws,
-                       size_t ws_bytes, void* stream, void* side_stream, void* fork_event,
-                       void* join_event) {
+                              float* logits, const moe4_w4* w13, const moe4_w4* w2,
+                              const moe4_w4* shared13, const moe4_w4* shared2, const uint16_t* residual,
+                              const uint16_t* gamma, int32_t* topk_idx, float* topk_w,
+                              uint16_t* residual_out, uint16_t* normed_out, void* ws, size_t ws_bytes,
+                              void* stream, void* side_stream, void* fork_event, void* join_event) {
   g_err[0] = 0;
   moe4_status st = check_shape(shape);
   if (st) return st;

@@ -27,8 +27,8 @@
 // The weights are read through the caches: every M-tile of an expert reads the same
 // weight tiles, and the tile order keeps those workgroups on one XCD. One barrier
 // per step. Each 16-wide K substep reads its operand fragments from LDS while
-// the previous one's MFMAs run. LDS rows are XOR-swizzled in 16-byte chunks so the
-// MFMA operand reads spread over the banks.
+// the previous one's MFMAs run. LDS rows are XOR-swizzled in 16-byte chunks so that
+// both the MFMA operand reads and the stores spread over the banks.
 //
 // Scheduling. One grid covers (expert M-tile, N-tile) pairs up to a bound; each
 // workgroup finds its expert by scanning the per-expert tile counts from the
@@ -64,8 +64,14 @@ struct GemmArgs {
   int total;                // grid size (multiple of kXcds)
 };
 
-// element offset of (row, 16-byte chunk) in a [rows][64] BF16 LDS tile
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3); }
+// LDS tiles are [rows][64] BF16, 128 bytes a row; the 16-byte chunk c of row r is stored
+// at chunk c ^ swz_key(r). The key keeps both access shapes free of bank conflicts (as
+// measured on gfx950): a 128-bit read serves 16 lanes at a time over 256 bytes of banks,
+// i.e. two rows, so the keys of the 8 even (and of the 8 odd) rows of an aligned group of
+// 16 must differ; a 128-bit write serves 8 lanes at a time over 128 bytes, so the weight
+// stores (8 lanes = 8 consecutive rows, same chunk) need 8 different keys on aligned
+// groups of 8 rows. The key depends only on r % 16.
+__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 template <bool kUp>
 __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
@@ -157,12 +163,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
     b_st[h] = blk * 16 + (l & 15);
   }
   const int b_kq = (tid & 31) >> 4;  // same for both units
-  // LDS swizzle: the 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7). For every
-  // row a lane touches, (r >> 1) & 7 depends only on the lane, so the addresses are a
+  // LDS swizzle (swz_key): for every row a lane touches, the key depends only on the
+  // lane (row offsets are multiples of 16), so the addresses are a
   // per-lane base plus immediate offsets.
-  const int a_sw = ((tid >> 3) >> 1) & 7;
+  const int a_sw = swz_key(tid >> 3);
   const int a_st = (tid >> 3) * BK + ((a_chunk ^ a_sw) << 3);  // + 64*i*BK for row group i
-  const int b_sw = ((tid & 15) >> 1) & 7;
+  const int b_sw = swz_key(tid & 15);
 
   // Two register sets, used by alternate steps: step s's data is loaded during step
   // s - 2 and written to LDS during step s - 1, so every load has a whole step and more
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   int boff[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) boff[j] = kUp ? 128 * j + 32 * wn : 64 * wn + 32 * j;
-  const int f_sw = (r32 >> 1) & 7;
+  const int f_sw = swz_key(r32);
   const int fa_base = (128 * wm + r32) * BK, fb_base = r32 * BK;
 
   f32x16 acc[4][2];

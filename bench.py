@@ -20,6 +20,10 @@ Two timed passes:
      duration give ``roofline.achieved``.
 The fp64 oracle is timed on the host on a bounded sample (``cpu_baseline``).
 Prints one JSON line.
+
+``--op add_rmsnorm|group_rmsnorm`` times one of the neighbouring RMSNorm glue
+launches instead (a step is one launch over the workload's T x H rows) and prints
+its own line.
 """
 from __future__ import annotations
 
@@ -50,6 +54,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--side-stream", choices=["on", "off"], default="off",
                     help="routed chain on a side stream beside the shared expert (moe4_layer_side)")
+    ap.add_argument("--op", choices=["layer", "add_rmsnorm", "group_rmsnorm"], default="layer",
+                    help="what a step is: the MoE layer (default), or one of the neighbouring "
+                         "RMSNorm glue launches over the workload's T x H rows")
+    ap.add_argument("--group", type=int, default=0, help="group_rmsnorm group size (0 = H / 8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB twice with torch (a plain copy of known size, for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -131,12 +139,130 @@ def cpu_baseline(inp, budget_s):
             "sample": f"{what}; numpy fp64 with BLAS limited to 1 thread; {t_used:.1f} s"}
 
 
+def glue_main(args):
+    """One RMSNorm glue launch per step over the workload's T x H rows (x, residual and
+    gamma drawn as for the layer); the launches run back to back between two events on
+    the stream. Input copies are rotated so that at least 1 GiB is touched, up to 16
+    copies: decode-sized rows then stay cache-resident, as they are after the previous
+    kernel wrote them, instead of each launch paying for fresh pages."""
+    import numpy as np
+    import torch
+
+    from bit_moe_expert_amd import binding as B
+    from bit_moe_expert_amd import workloads as wl
+
+    w = wl.workload(args.config)
+    T, H = w.T * w.chunks, w.H
+    G = args.group or H // 8
+    rng = np.random.default_rng(0)
+    x = wl.to_bf16_bits(rng.standard_normal((T, H)))
+    res = wl.to_bf16_bits(rng.standard_normal((T, H)))
+    gam = wl.to_bf16_bits(rng.uniform(0.5, 1.5, H))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16))).cuda()
+    add = args.op == "add_rmsnorm"
+    per_call = T * H * 2 * (4 if add else 2) + H * 2        # rows in and out, gamma
+    copies = min(16, max(1, math.ceil(MALL_DEFEAT_BYTES / per_call)))
+    bufs = []
+    for _ in range(copies):
+        bufs.append(dict(x=dev(x), r=dev(res) if add else None,
+                         o=torch.empty((T, H), dtype=torch.int16, device="cuda") if add else None,
+                         n=torch.empty((T, H), dtype=torch.int16, device="cuda")))
+    d_g = dev(gam)
+
+    def step(i):
+        b = bufs[i % copies]
+        if add:
+            B.moe4_add_rmsnorm(b["x"], b["r"], d_g, b["o"], b["n"], eps=w.eps)
+        else:
+            B.moe4_group_rmsnorm(b["x"], G, d_g, b["n"], eps=w.eps)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    eager_s = ev0.elapsed_time(ev1) / args.steps / 1e3
+    ref_n = bufs[0]["n"].clone()
+    # The same launches captured into a HIP graph and replayed: at decode sizes the eager
+    # loop measures the host's launch rate, the replay the GPU's.
+    per_graph = min(args.steps, 256)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for i in range(3):
+            step(i)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for i in range(per_graph):
+            step(i)
+    torch.cuda.synchronize()
+    replays = max(1, args.steps // per_graph)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    if not torch.equal(bufs[0]["n"], ref_n):
+        raise RuntimeError("graph replay output differs from the eager launch")
+    mean_s = ev0.elapsed_time(ev1) / (replays * per_graph) / 1e3
+    achieved = per_call / mean_s / 1e9
+    log(f"{args.op}: {mean_s * 1e6:.2f} us per launch in graph replay ({eager_s * 1e6:.2f} us eager), "
+        f"{achieved:.1f} GB/s, {copies} input copies")
+    desc = f"group={G}" if not add else "o = x + residual"
+    out = {"metric": f"{args.op} rows/s", "value": round(T / mean_s, 1), "unit": "rows/s", "n_gpus": 1,
+           "steps": replays * per_graph, "warmup": args.warmup, "ms_per_step": round(mean_s * 1e3, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": f"{args.op} over {T} rows of H={H} BF16 ({desc}), rows of the "
+                                  f"{args.config} workload; launches replayed from a HIP graph",
+                      "T": T, "H": H, "group": G if not add else H, "input_copies_rotated": copies,
+                      "eager_us_per_launch": round(eager_s * 1e6, 3)},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "rmsnorm_kernel", "mean_us": round(mean_s * 1e6, 3),
+                        "algorithmic_bytes": per_call}}
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = min(T, 64)
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            if add:
+                oracle.add_rmsnorm(x[:rows], res[:rows], gam, w.eps)
+            else:
+                oracle.group_rmsnorm(x[:rows], G, gam, w.eps)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > min(args.cpu_seconds, 5.0):
+                break
+        out["cpu_baseline"] = {"value": round(rows * reps / el, 1), "unit": "rows/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{rows} rows x {reps} repetitions"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (got --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    if args.op != "layer":
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        torch.cuda.set_device(0)
+        glue_main(args)
+        return
 
     import numpy as np
     import torch

@@ -55,6 +55,10 @@ SIGNATURES = {
     "moe4_layer_side": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, _W4, _W4, _W4, _W4, c_void_p,
                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                 c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe4_add_rmsnorm": (c_int, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_float, c_void_p,
+                                 c_void_p, c_void_p]),
+    "moe4_group_rmsnorm": (c_int, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_float, c_void_p,
+                                   c_void_p]),
 }
 
 ABI_VERSION = 1

@@ -150,6 +150,24 @@ def moe4_combine_norm(shape: Shape, y, inv, topk_w, shared_y, residual, gamma, r
         _ptr(normed_out, "normed_out", _BF16_LIKE, T * H), _stream(stream)))
 
 
+def moe4_add_rmsnorm(x, residual, gamma, residual_out, normed_out, eps: float = 1e-6,
+                     stream=None) -> None:
+    """residual_out = x + residual; normed_out = RMSNorm(residual_out) * gamma ([T][H] BF16)."""
+    T, H = x.shape
+    check(_lib.load().moe4_add_rmsnorm(
+        T, H, _ptr(x, "x", _BF16_LIKE, T * H), _ptr(residual, "residual", _BF16_LIKE, T * H),
+        _ptr(gamma, "gamma", _BF16_LIKE, H), eps, _ptr(residual_out, "residual_out", _BF16_LIKE, T * H),
+        _ptr(normed_out, "normed_out", _BF16_LIKE, T * H), _stream(stream)))
+
+
+def moe4_group_rmsnorm(x, group: int, gamma, normed_out, eps: float = 1e-6, stream=None) -> None:
+    """normed_out = x normalised over each group of ``group`` columns, times gamma."""
+    T, H = x.shape
+    check(_lib.load().moe4_group_rmsnorm(
+        T, H, group, _ptr(x, "x", _BF16_LIKE, T * H), _ptr(gamma, "gamma", _BF16_LIKE, H), eps,
+        _ptr(normed_out, "normed_out", _BF16_LIKE, T * H), _stream(stream)))
+
+
 def moe4_layer(shape: Shape, x, w_router, logits, w13: DeviceW4, w2: DeviceW4,
                shared13: Optional[DeviceW4], shared2: Optional[DeviceW4], residual, gamma,
                topk_idx, topk_w, residual_out, normed_out, ws, stream=None, side_stream=None,

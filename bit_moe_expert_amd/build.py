@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build", "moe4")
 LIB_PATH = os.path.join(HERE, "libmoe4.so")
 
-SOURCES = ["abi.hip", "route.hip", "permute.hip", "prepack.hip", "ffn_decode.hip", "ffn_prefill.hip", "combine.hip"]
+SOURCES = ["abi.hip", "route.hip", "permute.hip", "prepack.hip", "ffn_decode.hip", "ffn_prefill.hip", "combine.hip", "norm.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -294,6 +294,45 @@ moe4_status moe4_combine_norm(const moe4_shape* shape, const uint16_t* y, const 
   return MOE4_OK;
 }
 
+static moe4_status rmsnorm_impl(int32_t T, int32_t H, int32_t group, const uint16_t* x,
+                                const uint16_t* residual, const uint16_t* gamma, float eps,
+                                uint16_t* residual_out, uint16_t* normed_out, void* stream) {
+  if (T < 0 || H <= 0 || group <= 0)
+    return fail(MOE4_ERR_INVALID_ARG, "negative or zero size (T=%d H=%d group=%d)", T, H, group);
+  if (!moe4::rmsnorm_shape_ok(H, group))
+    return fail(MOE4_ERR_UNSUPPORTED, "H=%d must be a multiple of 8 in [8, 16384] and group=%d a multiple of 8 dividing it",
+                H, group);
+  if (T > (1 << 24)) return fail(MOE4_ERR_UNSUPPORTED, "T=%d > 2^24", T);
+  if (!(eps > 0.0f)) return fail(MOE4_ERR_INVALID_ARG, "eps must be > 0");
+  if (T == 0) return MOE4_OK;  // nothing to read or write
+  NEED(x, "x");
+  if (residual) NEED(residual, "residual");
+  NEED(gamma, "gamma");
+  if (residual_out) NEED(residual_out, "residual_out");
+  NEED(normed_out, "normed_out");
+  if (residual_out == normed_out) return fail(MOE4_ERR_INVALID_ARG, "residual_out and normed_out are the same buffer");
+  if (gamma == normed_out || gamma == residual_out) return fail(MOE4_ERR_INVALID_ARG, "gamma aliases an output");
+  hipError_t e = moe4::launch_rmsnorm(x, residual, gamma, residual_out, normed_out, T, H, group, eps,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+  return MOE4_OK;
+}
+
+moe4_status moe4_add_rmsnorm(int32_t T, int32_t H, const uint16_t* x, const uint16_t* residual,
+                             const uint16_t* gamma, float eps, uint16_t* residual_out,
+                             uint16_t* normed_out, void* stream) {
+  g_err[0] = 0;
+  if (T > 0 && residual == nullptr) return fail(MOE4_ERR_INVALID_ARG, "residual is NULL");
+  if (T > 0 && residual_out == nullptr) return fail(MOE4_ERR_INVALID_ARG, "residual_out is NULL");
+  return rmsnorm_impl(T, H, H, x, residual, gamma, eps, residual_out, normed_out, stream);
+}
+
+moe4_status moe4_group_rmsnorm(int32_t T, int32_t H, int32_t group, const uint16_t* x,
+                               const uint16_t* gamma, float eps, uint16_t* normed_out, void* stream) {
+  g_err[0] = 0;
+  return rmsnorm_impl(T, H, group, x, nullptr, gamma, eps, nullptr, normed_out, stream);
+}
+
 // The layer on `stream`, or with the routed chain on `side_stream` (see moe4_layer_side).
 static moe4_status layer_impl(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
                               float* logits, const moe4_w4* w13, const moe4_w4* w2,

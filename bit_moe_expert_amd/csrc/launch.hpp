@@ -61,4 +61,11 @@ hipError_t launch_combine_norm(const uint16_t* y, const int32_t* inv, const floa
                                const uint16_t* gamma, uint16_t* res_out, uint16_t* norm_out, int T,
                                int H, int k, float eps, hipStream_t s);
 
+// o = x (+ residual); n = o / rms(o over each group of `group` columns) * gamma.
+// res_out may be NULL. Needs rmsnorm_shape_ok(H, group).
+bool rmsnorm_shape_ok(int H, int group);
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* gamma,
+                          uint16_t* res_out, uint16_t* norm_out, int T, int H, int group, float eps,
+                          hipStream_t s);
+
 }  // namespace moe4

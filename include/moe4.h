@@ -221,6 +221,33 @@ moe4_status moe4_layer_side(const moe4_shape* shape, const uint16_t* x, const ui
                             size_t ws_bytes, void* stream, void* side_stream, void* fork_event,
                             void* join_event);
 
+/* Neighbouring glue: the two RMSNorm launches of a decode step beside the MoE layer
+ * (#627: add_rmsnorm in the Oct 10 list of the other glue ops, add_rmsnorm and
+ * group_rmsnorm in the Oct 14 per-step breakdown). Neither takes a moe4_shape.
+ * Constraints: 0 <= T <= 2^24 (T == 0 does nothing); H a multiple of 8 in [8, 16384]; eps > 0;
+ * pointers 16-byte aligned; gamma must not alias an output; each output may alias any
+ * input (every element is read before it is written), the two outputs must differ.
+ *
+ * add_rmsnorm: the residual add and RMSNorm in front of attention.
+ *   x, residual  BF16 [T][H] in.
+ *   gamma        BF16 [H].
+ *   residual_out BF16 [T][H] out: o = x + residual (FP32 sum, rounded to BF16).
+ *   normed_out   BF16 [T][H] out: o / sqrt(mean(o^2) + eps) * gamma from the FP32 o. */
+moe4_status moe4_add_rmsnorm(int32_t T, int32_t H, const uint16_t* x, const uint16_t* residual,
+                             const uint16_t* gamma, float eps, uint16_t* residual_out,
+                             uint16_t* normed_out, void* stream);
+
+/* group_rmsnorm: RMSNorm over contiguous groups of `group` columns of each row (the
+ * pages name the launch only; read here as each group normalised by its own mean
+ * square, then one gamma over the row, with no gate).
+ *   x          BF16 [T][H] in.
+ *   group      columns per group: a multiple of 8 that divides H (group == H is a plain
+ *              RMSNorm).
+ *   gamma      BF16 [H].
+ *   normed_out BF16 [T][H] out: x / sqrt(mean over x's group(x^2) + eps) * gamma. */
+moe4_status moe4_group_rmsnorm(int32_t T, int32_t H, int32_t group, const uint16_t* x,
+                               const uint16_t* gamma, float eps, uint16_t* normed_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,6 +35,13 @@ Readings where the pages are silent (each is stated again where it is used):
       hidden h (the down projection's input) and the expert output y are rounded to
       BF16 (nearest, ties to even); every sum and the combine/norm are fp64, and the
       layer outputs o and n are left unrounded.
+  R16 add_rmsnorm (#627, the Oct 10 list of the other glue ops and the Oct 14
+      per-step breakdown name it without defining it) is the residual add in front
+      of attention followed by the RMSNorm of R10: o = x + residual, n = o / rms(o) *
+      gamma; both o and n are outputs.
+  R17 group_rmsnorm (named the same way) normalises each contiguous group of G
+      columns of a row by that group's own mean square, then multiplies by one gamma
+      over the whole row; there is no gate (the pages name none). G = H is R10.
 
 Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
 (closed forms, library routines, brute force on tiny inputs, invariants).
@@ -46,7 +53,7 @@ import numpy as np
 __all__ = [
     "bf16_value", "bf16_round", "e2m1_value", "e4m3_value", "unpack_codes", "dequant",
     "router_logits", "route", "permute", "swiglu_hidden", "swiglu_ffn", "expert_outputs",
-    "combine_norm", "layer",
+    "combine_norm", "add_rmsnorm", "group_rmsnorm", "layer",
 ]
 
 
@@ -243,6 +250,34 @@ def combine_norm(y, w, residual_bits, gamma_bits, eps, shared=None):
     ms = np.mean(o * o, axis=1, keepdims=True)
     n = o / np.sqrt(ms + eps) * bf16_value(gamma_bits)[None, :]
     return o, n
+
+
+# ----------------------------------------------------------------------------
+# The neighbouring RMSNorm glue (add_rmsnorm, group_rmsnorm), readings R16, R17
+# ----------------------------------------------------------------------------
+def group_rmsnorm(x_bits, group, gamma_bits, eps):
+    """n[t, h] = x[t, h] / sqrt(mean of x[t, .]^2 over h's group + eps) * gamma[h].
+
+    x_bits BF16 [T, H] (or fp64 values: anything that is not uint16 is taken as
+    values), group divides H; returns fp64 [T, H].
+    """
+    x = np.asarray(x_bits)
+    x = bf16_value(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    T, H = x.shape
+    if group <= 0 or H % group:
+        raise ValueError(f"group {group} does not divide H={H}")
+    n = np.empty_like(x)
+    for g0 in range(0, H, group):
+        seg = x[:, g0:g0 + group]
+        ms = np.mean(seg * seg, axis=1, keepdims=True)
+        n[:, g0:g0 + group] = seg / np.sqrt(ms + eps)
+    return n * bf16_value(gamma_bits)[None, :]
+
+
+def add_rmsnorm(x_bits, residual_bits, gamma_bits, eps):
+    """o = x + residual; n = o / sqrt(mean(o^2) + eps) * gamma (fp64 [T, H] each)."""
+    o = bf16_value(x_bits) + bf16_value(residual_bits)
+    return o, group_rmsnorm(o, o.shape[1], gamma_bits, eps)
 
 
 # ----------------------------------------------------------------------------

@@ -147,3 +147,31 @@ def test_prepack_checks():
     assert lib.moe4_prepack_w4(-1, 64, 256, FAKE, FAKE, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
     assert lib.moe4_prepack_w4(1, 64, 256, None, FAKE, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
     assert lib.moe4_prepack_w4(0, 64, 256, None, None, None, None, None) == _lib.MOE4_OK
+
+
+def test_rmsnorm_glue_checks():
+    """add_rmsnorm / group_rmsnorm reject bad sizes and pointers before any launch."""
+    lib = _lib.load()
+    E_ARG, E_UNS, OK = _lib.MOE4_ERR_INVALID_ARG, _lib.MOE4_ERR_UNSUPPORTED, _lib.MOE4_OK
+    out2 = ctypes.c_void_p(0x3000)
+    # sizes
+    assert lib.moe4_add_rmsnorm(-1, 64, FAKE, FAKE, FAKE, 1e-6, FAKE, out2, None) == E_ARG
+    assert lib.moe4_add_rmsnorm(4, 60, FAKE, FAKE, FAKE, 1e-6, FAKE, out2, None) == E_UNS
+    assert lib.moe4_add_rmsnorm(4, 16392, FAKE, FAKE, FAKE, 1e-6, FAKE, out2, None) == E_UNS
+    assert lib.moe4_add_rmsnorm(4, 64, FAKE, FAKE, FAKE, 0.0, FAKE, out2, None) == E_ARG
+    assert lib.moe4_group_rmsnorm(4, 64, 12, FAKE, FAKE, 1e-6, FAKE, None) == E_UNS   # not a multiple of 8
+    assert lib.moe4_group_rmsnorm(4, 64, 48, FAKE, FAKE, 1e-6, FAKE, None) == E_UNS   # does not divide H
+    assert lib.moe4_group_rmsnorm(4, 64, 0, FAKE, FAKE, 1e-6, FAKE, None) == E_ARG
+    # pointers
+    assert lib.moe4_add_rmsnorm(4, 64, None, FAKE, FAKE, 1e-6, FAKE, out2, None) == E_ARG
+    assert lib.moe4_add_rmsnorm(4, 64, FAKE, None, FAKE, 1e-6, FAKE, out2, None) == E_ARG
+    assert lib.moe4_add_rmsnorm(4, 64, FAKE, FAKE, FAKE, 1e-6, None, out2, None) == E_ARG
+    assert lib.moe4_add_rmsnorm(4, 64, FAKE, FAKE, ctypes.c_void_p(0x1008), 1e-6, FAKE, out2, None) == E_ARG
+    assert b"gamma" in lib.moe4_last_error()
+    assert lib.moe4_add_rmsnorm(4, 64, FAKE, FAKE, FAKE, 1e-6, out2, out2, None) == E_ARG
+    assert b"same buffer" in lib.moe4_last_error()
+    assert lib.moe4_group_rmsnorm(4, 64, 16, FAKE, out2, 1e-6, out2, None) == E_ARG
+    assert b"gamma aliases" in lib.moe4_last_error()
+    # T == 0 does nothing, NULL buffers included
+    assert lib.moe4_add_rmsnorm(0, 64, None, None, None, 1e-6, None, None, None) == OK
+    assert lib.moe4_group_rmsnorm(0, 64, 16, None, None, 1e-6, None, None) == OK

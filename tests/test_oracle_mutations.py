@@ -102,6 +102,29 @@ def _combine_shared_dropped(y, w, residual_bits, gamma_bits, eps, shared=None):
     return _orig["combine_norm"](y, w, residual_bits, gamma_bits, eps, None)
 
 
+def _group_norm_whole_row(x_bits, group, gamma_bits, eps):  # the group ignored
+    x = np.asarray(x_bits)
+    return _orig["group_rmsnorm"](x_bits, x.shape[1], gamma_bits, eps)
+
+
+def _group_norm_no_eps(x_bits, group, gamma_bits, eps):
+    return _orig["group_rmsnorm"](x_bits, group, gamma_bits, 0.0)
+
+
+def _group_norm_gamma_per_group(x_bits, group, gamma_bits, eps):  # gamma[h % group]
+    g = np.asarray(gamma_bits)
+    return _orig["group_rmsnorm"](x_bits, group, np.tile(g[:group], g.shape[0] // group), eps)
+
+
+def _add_norm_of_x(x_bits, residual_bits, gamma_bits, eps):  # normalises x, not x + residual
+    o, _ = _orig["add_rmsnorm"](x_bits, residual_bits, gamma_bits, eps)
+    return o, oracle.group_rmsnorm(x_bits, o.shape[1], gamma_bits, eps)
+
+
+def _add_norm_no_residual(x_bits, residual_bits, gamma_bits, eps):
+    return _orig["add_rmsnorm"](x_bits, np.zeros_like(residual_bits), gamma_bits, eps)
+
+
 def _bf16_truncate(v):
     v = np.asarray(v, dtype=np.float64)
     _, e = np.frexp(v)
@@ -124,6 +147,8 @@ MUTANTS = {
     "swiglu_hidden": [_hidden_swapped, _hidden_no_silu],
     "swiglu_ffn": [_swiglu_swapped, _swiglu_w2_transposed_use, _ffn_unrounded],
     "combine_norm": [_combine_no_residual, _combine_no_gamma, _combine_shared_dropped],
+    "group_rmsnorm": [_group_norm_whole_row, _group_norm_no_eps, _group_norm_gamma_per_group],
+    "add_rmsnorm": [_add_norm_of_x, _add_norm_no_residual],
 }
 
 CASES = [(name, fn) for name, fns in MUTANTS.items() for fn in fns]

@@ -343,6 +343,69 @@ def test_combine_norm_closed_forms():
 
 
 # ----------------------------------------------------------------------------
+# RMSNorm glue: add_rmsnorm and group_rmsnorm
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("group", [8, 24, 96])
+def test_group_rmsnorm_matches_torch_rms_norm_per_group(group):
+    # the library routine applied to each group's slice (a reshape), gamma after it
+    rng = np.random.default_rng(11)
+    T, H = 5, 96
+    x = wl.to_bf16_bits(rng.standard_normal((T, H)) * rng.uniform(0.1, 10, (T, 1)))
+    gam = wl.to_bf16_bits(rng.uniform(0.5, 1.5, H))
+    n = oracle.group_rmsnorm(x, group, gam, 1e-6)
+    xv = torch.from_numpy(oracle.bf16_value(x)).reshape(T, H // group, group)
+    ref = torch.nn.functional.rms_norm(xv, (group,), eps=1e-6).reshape(T, H)
+    ref = ref * torch.from_numpy(oracle.bf16_value(gam))
+    np.testing.assert_allclose(n, ref.numpy(), rtol=1e-13, atol=1e-14)
+
+
+def test_add_rmsnorm_matches_torch_rms_norm():
+    rng = np.random.default_rng(12)
+    T, H = 6, 128
+    x = wl.to_bf16_bits(rng.standard_normal((T, H)))
+    res = wl.to_bf16_bits(rng.standard_normal((T, H)))
+    gam = wl.to_bf16_bits(rng.uniform(0.5, 1.5, H))
+    o, n = oracle.add_rmsnorm(x, res, gam, 1e-6)
+    # the sum of two BF16 values is exact in fp64
+    o_ref = torch.from_numpy(oracle.bf16_value(x)) + torch.from_numpy(oracle.bf16_value(res))
+    np.testing.assert_array_equal(o, o_ref.numpy())
+    n_ref = torch.nn.functional.rms_norm(o_ref, (H,), weight=torch.from_numpy(oracle.bf16_value(gam)), eps=1e-6)
+    np.testing.assert_allclose(n, n_ref.numpy(), rtol=1e-13, atol=1e-14)
+
+
+def test_group_rmsnorm_closed_forms():
+    ones = wl.to_bf16_bits(np.ones(32))
+    # a constant group c: every value becomes sign(c) (eps small against c^2)
+    x = np.concatenate([np.full(8, -3.0), np.full(8, 0.5), np.full(16, 2.0)])[None, :]
+    n = oracle.group_rmsnorm(wl.to_bf16_bits(x), 8, ones, 1e-30)
+    np.testing.assert_allclose(n[0], np.sign(x[0]), rtol=1e-14)
+    # one group of size H is the plain norm; groups differing only by a power-of-two
+    # scale normalise to the same values
+    rng = np.random.default_rng(13)
+    v = rng.standard_normal(8)
+    x2 = np.concatenate([v, 4 * v, 0.25 * v, v])[None, :]
+    n2 = oracle.group_rmsnorm(wl.to_bf16_bits(x2), 8, ones, 1e-30)
+    for g in range(1, 4):
+        np.testing.assert_allclose(n2[0, 8 * g:8 * g + 8], n2[0, :8], rtol=1e-12)
+    # gamma = 1: each group's rms is 1
+    x3 = wl.to_bf16_bits(rng.standard_normal((3, 32)))
+    n3 = oracle.group_rmsnorm(x3, 16, ones, 1e-30).reshape(3, 2, 16)
+    np.testing.assert_allclose(np.sqrt(np.mean(n3 * n3, axis=2)), 1.0, rtol=1e-12)
+    # a brute-force pure-Python loop on a tiny row with eps mattering
+    xs = [1.0, -2.0, 0.5, 4.0, 0.0, 0.0, 0.0, 0.0]
+    gs = [1.0, 0.5, 2.0, 1.5, 1.0, 1.0, 1.0, 1.0]
+    eps = 0.25
+    want = []
+    for g0 in (0, 4):
+        ms = sum(v * v for v in xs[g0:g0 + 4]) / 4
+        want += [xs[h] / math.sqrt(ms + eps) * gs[h] for h in range(g0, g0 + 4)]
+    got = oracle.group_rmsnorm(wl.to_bf16_bits(np.array([xs])), 4, wl.to_bf16_bits(np.array(gs)), eps)
+    np.testing.assert_allclose(got[0], want, rtol=1e-15, atol=0)
+    with pytest.raises(ValueError):
+        oracle.group_rmsnorm(x3, 12, ones, 1e-6)
+
+
+# ----------------------------------------------------------------------------
 # Whole layer: per-token independence
 # ----------------------------------------------------------------------------
 def test_layer_rows_are_independent_of_batch():

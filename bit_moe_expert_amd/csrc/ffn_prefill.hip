@@ -31,10 +31,12 @@
 // both the MFMA operand reads and the stores spread over the banks.
 //
 // Scheduling. One grid covers (expert M-tile, N-tile) pairs up to a bound; each
-// workgroup finds its expert by scanning the per-expert tile counts from the
-// offsets. Workgroup ids are remapped so each XCD (ids are dealt round-robin to the
-// 8 XCDs) gets a contiguous run of tiles with N fastest: the workgroups sharing an
-// activation tile, and an expert's weights, meet in the same L2.
+// workgroup counts the per-expert tiles from the offsets, which gives the number of
+// real tiles and its own expert. The real tiles are dealt to the 8 XCDs (workgroup
+// ids go round-robin to them) in equal contiguous runs with N fastest: the workgroups
+// sharing an activation tile, and an expert's weights, meet in the same L2, and every
+// XCD gets the same share of work. (Dealing the bound's range instead left the last
+// XCDs with only empty tiles: at prefill about a sixth of the CUs idled.)
 #include <type_traits>
 
 #include "device.hpp"
@@ -47,6 +49,7 @@ namespace {
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 512;
 constexpr int kXcds = 8;
+constexpr int kMaxExperts = 256;  // the ABI's bound on G
 
 struct GemmArgs {
   const uint16_t* act;      // up: x [T][H]; down: h [R][I]
@@ -77,57 +80,117 @@ template <bool kUp>
 __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BN * BK];
-  __shared__ int sched[3];
+  __shared__ int sched[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // XCD-aware remap of the workgroup id to a logical tile, N fastest
-  const int per_xcd = a.total / kXcds;
-  const int Q = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int mtile = Q / a.n_tiles, nt = Q % a.n_tiles;
 
-  // expert and row range of M-tile `mtile`
+  // Tile schedule. An expert's M-tiles are full tiles (more than 128 rows) and at most
+  // one half tile (its last, of at most 128 rows, which only the four waves of rows
+  // 0..127 compute). Wave 0 counts both kinds per expert (inclusive prefixes over the
+  // experts, 64 a round, kept in registers). The grid is sized from a bound; the real
+  // tiles are dealt to the 8 XCDs (workgroup ids go round-robin to them), each kind in
+  // equal contiguous runs with N fastest: XCD x runs its share of the full tiles, then
+  // its share of the half tiles. So the workgroups sharing an activation tile, and an
+  // expert's weights, meet in the same L2, every XCD gets the same amount of work
+  // whatever the routing, and each XCD ends on short tiles. Workgroups past their XCD's
+  // runs exit at once. (Dealing the bound's range in one run left the last XCDs with
+  // empty tiles, and XCDs with the small experts ran out early: about a fifth of the
+  // CU time idled at prefill.)
   if (wave == 0) {
-    int g = -1, r0 = 0, M = 0, mt = 0;
+    int g = -1, r0 = 0, rows = 0, nt = 0;
+    const int j = blockIdx.x / kXcds, x = blockIdx.x % kXcds;
     if (a.offsets) {
-      int carry = 0;
-      for (int base = 0; base < a.G && g < 0; base += 64) {
-        const int e = base + lane;
+      int incl_f[kMaxExperts / 64], incl_h[kMaxExperts / 64];
+      int carry_f = 0, carry_h = 0;
+#pragma unroll
+      for (int c = 0; c < kMaxExperts / 64; ++c) {
+        const int e = 64 * c + lane;
         const int cnt = e < a.G ? a.offsets[e + 1] - a.offsets[e] : 0;
-        const int tiles = (cnt + BM - 1) / BM;
-        int incl = tiles;
+        int f = cnt / BM + (cnt % BM > BM / 2 ? 1 : 0);
+        int h = (cnt % BM != 0 && cnt % BM <= BM / 2) ? 1 : 0;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-          const int o = __shfl_up(incl, off);
-          if (lane >= off) incl += o;
+          const int of = __shfl_up(f, off), oh = __shfl_up(h, off);
+          if (lane >= off) {
+            f += of;
+            h += oh;
+          }
         }
-        const int excl = carry + incl - tiles;
-        const uint64_t hit = __ballot(e < a.G && tiles > 0 && mtile >= excl && mtile < excl + tiles);
-        if (hit) {
-          const int src = __ffsll((long long)hit) - 1;
-          g = __shfl(e, src);
-          mt = mtile - __shfl(excl, src);
-        }
-        carry += __shfl(incl, 63);
+        incl_f[c] = carry_f + f;
+        incl_h[c] = carry_h + h;
+        carry_f += __shfl(f, 63);
+        carry_h += __shfl(h, 63);
       }
-      if (g >= 0) {
-        r0 = a.offsets[g];
-        M = a.offsets[g + 1] - r0;
+      const int n_f = carry_f * a.n_tiles, n_h = carry_h * a.n_tiles;
+      const int per_f = (n_f + kXcds - 1) / kXcds, per_h = (n_h + kXcds - 1) / kXcds;
+      // this workgroup's tile: class (full / half), index of the M-tile within the class
+      int q = -1, half = 0;
+      if (j < per_f) {
+        q = x * per_f + j;
+        if (q >= n_f) q = -1;
+      } else if (j - per_f < per_h) {
+        q = x * per_h + (j - per_f);
+        half = 1;
+        if (q >= n_h) q = -1;
+      }
+      if (q >= 0) {
+        const int m = q / a.n_tiles;
+        nt = q % a.n_tiles;
+#pragma unroll
+        for (int c = 0; c < kMaxExperts / 64; ++c) {
+          const int e = 64 * c + lane;
+          const int incl = half ? incl_h[c] : incl_f[c];
+          const int prev = __shfl_up(incl, 1);  // every lane takes part in both shuffles
+          const int before = c == 0 ? 0 : __shfl(half ? incl_h[c > 0 ? c - 1 : 0] : incl_f[c > 0 ? c - 1 : 0], 63);
+          const int excl = lane == 0 ? before : prev;
+          const uint64_t hit = __ballot(e < a.G && m >= excl && m < incl);
+          if (hit && g < 0) {
+            const int src = __ffsll((long long)hit) - 1;
+            g = __shfl(e, src);
+            const int mt = half ? 0 : m - __shfl(excl, src);
+            r0 = a.offsets[g];
+            const int cnt = a.offsets[g + 1] - r0;
+            // a half tile is the expert's last M-tile
+            const int m0 = half ? cnt / BM : mt;
+            r0 += m0 * BM;
+            rows = min(BM, cnt - m0 * BM);
+          }
+        }
       }
     } else {
-      g = 0;
-      M = a.T;
-      mt = mtile;
-      if (mt * BM >= M) g = -1;
+      // dense: one group of T rows
+      const int cnt = a.T;
+      const int n_f = (cnt / BM + (cnt % BM > BM / 2 ? 1 : 0)) * a.n_tiles;
+      const int n_h = ((cnt % BM != 0 && cnt % BM <= BM / 2) ? 1 : 0) * a.n_tiles;
+      const int per_f = (n_f + kXcds - 1) / kXcds, per_h = (n_h + kXcds - 1) / kXcds;
+      int q = -1, half = 0;
+      if (j < per_f) {
+        q = x * per_f + j;
+        if (q >= n_f) q = -1;
+      } else if (j - per_f < per_h) {
+        q = x * per_h + (j - per_f);
+        half = 1;
+        if (q >= n_h) q = -1;
+      }
+      if (q >= 0) {
+        g = 0;
+        nt = q % a.n_tiles;
+        const int m0 = half ? cnt / BM : q / a.n_tiles;
+        r0 = m0 * BM;
+        rows = min(BM, cnt - m0 * BM);
+      }
     }
     if (lane == 0) {
       sched[0] = g;
-      sched[1] = r0 + mt * BM;  // first row of the tile
-      sched[2] = min(BM, M - mt * BM);
+      sched[1] = r0;  // first row of the tile
+      sched[2] = rows;
+      sched[3] = nt;
     }
   }
   __syncthreads();
   const int g = sched[0];
-  if (g < 0 || Q >= a.total) return;
+  if (g < 0) return;
+  const int nt = sched[3];
   const int row0 = sched[1], rows = sched[2];
 
   const int K = a.K, NS = K / 128, NB = a.N / 16, nsteps = K / BK;
@@ -315,7 +378,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
 hipError_t launch(bool up, GemmArgs a, long long m_tiles, hipStream_t s) {
   a.n_tiles = up ? a.I / 128 : a.N / BN;
   const long long tiles = m_tiles * a.n_tiles;
-  a.total = (int)((tiles + kXcds - 1) / kXcds * kXcds);
+  // each of the two runs of an XCD (full tiles, half tiles) may round up by one
+  a.total = (int)((tiles + kXcds - 1) / kXcds * kXcds) + 2 * kXcds;
   if (up) hipLaunchKernelGGL(ffn_prefill_kernel<true>, dim3(a.total), dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(ffn_prefill_kernel<false>, dim3(a.total), dim3(kThreads), 0, s, a);
   return hipGetLastError();

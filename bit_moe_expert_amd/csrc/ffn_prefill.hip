@@ -317,6 +317,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
       copy_step(S1{}, st);
       copy_step(S0{}, st + 1);
     }
+    __syncthreads();  // the epilogue's barrier
     return;
   }
   read_frags(0, 0, fa, fb);
@@ -351,27 +352,39 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   }
 
   // ---- epilogue: acc[i][j][r] is row 8(r/4) + 4kh + r%4, column r32 of block (i, j) ----
+  // The wave's outputs go through LDS (the operand buffers are free once every wave has
+  // passed the barrier), so that each lane writes whole 16-byte row pieces: 8 (up) or 16
+  // (down) stores a wave instead of 64 or 128 of 2 bytes. A wave's LDS region is its own
+  // [128][W] BF16 block (W = 32 h columns for up, 64 y columns for down).
+  __syncthreads();
+  constexpr int W = kUp ? 32 : 64;
+  uint16_t* stage = (wave < 4 ? &lds_a[0][0] : &lds_b[0][0]) + (wave & 3) * (128 * W);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int tr = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
-      if (tr < rows) {
-        const size_t orow = (size_t)(row0 + tr);
-        if (kUp) {
-          {
-            const int col = nt * 128 + 32 * wn + r32;
-            a.out[orow * a.I + col] = f32_to_bf16(silu_mul(ts * acc[i][0][r], ts * acc[i][1][r]));
-          }
-        } else {
+      const int lr = 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (kUp) {
+        stage[lr * W + r32] = f32_to_bf16(silu_mul(ts * acc[i][0][r], ts * acc[i][1][r]));
+      } else {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = nt * BN + 64 * wn + 32 * j + r32;
-            a.out[orow * a.N + col] = f32_to_bf16(ts * acc[i][j][r]);
-          }
-        }
+        for (int j = 0; j < 2; ++j) stage[lr * W + 32 * j + r32] = f32_to_bf16(ts * acc[i][j][r]);
       }
     }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int kPieces = 128 * W / 8;  // 16-byte pieces of the wave's block
+  const size_t ld = kUp ? a.I : a.N;
+  const int col0 = kUp ? nt * 128 + 32 * wn : nt * BN + 64 * wn;
+#pragma unroll
+  for (int c = 0; c < kPieces / 64; ++c) {
+    const int piece = 64 * c + lane, lr = piece / (W / 8), lc = (piece % (W / 8)) * 8;
+    const int tr = 128 * wm + lr;
+    if (tr < rows)
+      *reinterpret_cast<u32x4*>(a.out + (size_t)(row0 + tr) * ld + col0 + lc) =
+          *reinterpret_cast<const u32x4*>(stage + lr * W + lc);
   }
 }
 

@@ -292,9 +292,32 @@ def test_expert_ffn_tile_edges():
     _check_routed_ffn(inp, w, off, perm)
 
 
-def test_expert_ffn_dense_shared():
-    w = wl.Workload("shared_small", T=77, H=1024, E=1, k=1, I=512, routing="normal")
-    note("expert ffn dense (shared expert mode) T=77")
+def test_expert_ffn_prefill_schedule_edges():
+    """The prefill GEMM's tile schedule over 256 experts, most of them empty: rows only
+    at the ends of the 64-expert rounds of its per-expert count (experts 0, 63, 64, 127,
+    128, 191, 255), groups that give half tiles (1, 100 rows and a 109-row tail), padded
+    full tiles (129) and both (300, 385), and few tiles per XCD for the down GEMM (one N
+    tile)."""
+    counts = np.zeros(256, dtype=np.int64)
+    for e, c in {0: 100, 63: 129, 64: 300, 127: 256, 128: 1, 191: 385}.items():
+        counts[e] = c
+    T = 64 * 256  # k = 1: as many rows as the prefill kernel needs over 256 experts
+    counts[255] = T - counts.sum()
+    w = wl.Workload("sched_edges", T=T, H=256, E=256, k=1, I=256, routing="normal")
+    note(f"expert ffn prefill schedule edges: groups {dict((int(e), int(c)) for e, c in enumerate(counts) if c)}")
+    inp = wl.make_inputs(w, seed=4)
+    idx = np.random.default_rng(6).permutation(np.repeat(np.arange(w.E), counts)).astype(np.int32)[:, None]
+    off, perm, inv = oracle.permute(idx, w.E)
+    assert np.array_equal(np.diff(off), counts)
+    _check_routed_ffn(inp, w, off, perm)
+
+
+@pytest.mark.parametrize("T", [77, 200, 300])
+def test_expert_ffn_dense_shared(T):
+    """Dense (shared expert) mode on the prefill GEMM: one half tile (77 rows), one
+    padded full tile (200) and a full tile plus a half one (300)."""
+    w = wl.Workload("shared_small", T=T, H=1024, E=1, k=1, I=512, routing="normal")
+    note(f"expert ffn dense (shared expert mode) T={T}")
     inp = wl.make_inputs(w, seed=2)
     shape = B.make_shape(inp.T, w.H, 1, 1, w.I)
     w13, w2, *_ = upload_weights(inp)

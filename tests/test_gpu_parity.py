@@ -486,6 +486,15 @@ def test_layer_deterministic_and_batch_independent():
     assert np.array_equal(c["idx"][0], a["idx"][3])
     assert np.array_equal(c["o_bits"][0], a["o_bits"][3])
     assert np.array_equal(c["n_bits"][0], a["n_bits"][3])
+    # and inside a batch of 9 (72 routed rows: the down projection stages its rows in LDS
+    # as FP16, where 8 tokens read them from the cache as BF16; the bits must not change)
+    nine = dataclasses.replace(inp, x=np.concatenate([inp.x, inp.x[5:6]]),
+                               residual=np.concatenate([inp.residual, inp.residual[5:6]]))
+    g9 = GpuLayer(nine, weights=(g.w13, g.w2, None, None, g.w_router))
+    g9.run()
+    d = g9.host()
+    assert np.array_equal(d["idx"][:8], a["idx"])
+    assert np.array_equal(d["o_bits"][:8], a["o_bits"]) and np.array_equal(d["n_bits"][:8], a["n_bits"])
 
 
 # moe4_layer takes the fused top-k + plan launch for small batches and may pick other

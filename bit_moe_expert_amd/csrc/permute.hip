@@ -109,6 +109,70 @@ __device__ void plan_single(const int32_t* flat, int n, int E, int32_t* __restri
     scatter_round(flat, base, n, E, run, wcnt, perm_src, inv);
 }
 
+// The plan of at most 64 pairs by one wave, without block barriers: lane f holds pair
+// f's expert; the counts go through LDS atomics, their exclusive scan gives the
+// offsets (each lane sums 4 consecutive experts, then a wave scan), and a pair's row
+// is its expert's offset plus its rank among the lower lanes with the same expert
+// (the stable order). `flat` is in LDS; `start` is E ints of LDS scratch.
+__device__ void plan_wave(const int* flat, int n, int E, int32_t* __restrict__ offsets,
+                          int32_t* __restrict__ perm_src, int32_t* __restrict__ inv, int* start) {
+  const int lane = threadIdx.x & 63;
+  const int e = lane < n ? flat[lane] : -1;
+  for (int i = lane; i < E; i += kWave) start[i] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (e >= 0) atomicAdd(&start[e], 1);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // experts 4*lane .. 4*lane+3 (E <= 256)
+  int c[4], sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = 4 * lane + j;
+    c[j] = x < E ? start[x] : 0;
+    sum += c[j];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  int pre = incl - sum;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = 4 * lane + j;
+    if (x < E) {
+      start[x] = pre;
+      offsets[x] = pre;
+    }
+    pre += c[j];
+  }
+  if (lane == 63) offsets[E] = incl;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // lanes with the same expert (9 bits: 0..255 and -1 differ)
+  uint64_t peers = ~0ull;
+#pragma unroll
+  for (int bit = 0; bit < 9; ++bit) {
+    const int v = (e >> bit) & 1;
+    const uint64_t bal = __ballot(v);
+    peers &= v ? bal : ~bal;
+  }
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  if (e >= 0) {
+    const int dest = start[e] + __popcll(peers & below);
+    perm_src[dest] = lane;
+    inv[lane] = dest;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void permute_single_kernel(const int32_t* __restrict__ flat,
                                                                   int n, int E,
                                                                   int32_t* __restrict__ offsets,
@@ -123,7 +187,9 @@ __global__ __launch_bounds__(kThreads) void permute_single_kernel(const int32_t*
 
 // Top-k of every token (wave w takes tokens w, w + 16, ...) followed by the plan, in
 // one workgroup: one launch instead of two for small batches. The selections are
-// kept in LDS for the plan and written out as the routing outputs.
+// kept in LDS for the plan and written out as the routing outputs. Up to 64 pairs
+// (decode up to T*k = 64) the plan is one wave's (plan_wave), without the block
+// barriers of the histogram, scan and scatter rounds.
 __global__ __launch_bounds__(kThreads) void route_plan_kernel(const float* __restrict__ logits, int T,
                                                               int E, int k, int32_t* __restrict__ idx,
                                                               float* __restrict__ w,
@@ -147,6 +213,10 @@ __global__ __launch_bounds__(kThreads) void route_plan_kernel(const float* __res
     }
   }
   __syncthreads();
+  if (T * k <= kWave) {
+    if (wave == 0) plan_wave(sidx, T * k, E, offsets, perm_src, inv, cnt);
+    return;
+  }
   plan_single(sidx, T * k, E, offsets, perm_src, inv, cnt, run, wcnt, lds4);
 }
 

@@ -546,6 +546,18 @@ def test_layer_matches_entry_points(name, w):
     assert np.array_equal(tw.cpu().numpy().view(np.int32), g.topk_w.cpu().numpy().view(np.int32))
     assert np.array_equal(to_host_bits(o), a["o_bits"])
     assert np.array_equal(to_host_bits(nrm), a["n_bits"])
+    # The layer's own plan (white box: the layer keeps offsets, perm_src and inv at the
+    # start of its workspace, each padded to 256 bytes) is the oracle's stable plan,
+    # whichever of the fused top-k + plan forms built it.
+    pad = lambda v: (v + 255) // 256 * 256
+    ws = g.ws.cpu().numpy()
+    p0 = pad((E + 1) * 4)
+    i0 = p0 + pad(T * k * 4)
+    ref_off, ref_perm, ref_inv = oracle.permute(a["idx"], E)
+    assert np.array_equal(ws[:(E + 1) * 4].view(np.int32), ref_off)
+    assert np.array_equal(ws[p0:p0 + T * k * 4].view(np.int32), ref_perm)
+    assert np.array_equal(ws[i0:i0 + T * k * 4].view(np.int32), ref_inv)
+    assert np.array_equal(off.cpu().numpy(), ref_off) and np.array_equal(perm.cpu().numpy(), ref_perm)
 
 
 GRAPH_CASES = [

@@ -17,7 +17,7 @@
 // rows are 128 gate rows and the matching 128 up rows, and each wave takes 32 of each,
 // so gate and up accumulators of the same h columns sit in the same lanes and SwiGLU
 // is applied in registers. An expert's last tile, when it has at most 128 rows, is
-// computed by the four waves of rows 0..127 alone; the other four only help fill LDS.
+// computed by all eight waves as 64 x 64 tiles, again two waves per SIMD.
 //
 // Pipeline. Activation rows (gathered through perm_src for the up projection) and
 // weight half-tiles (tiled layout, 512 contiguous bytes per 16-row block) are loaded
@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // Tile schedule. An expert's M-tiles are full tiles (more than 128 rows) and at most
-  // one half tile (its last, of at most 128 rows, which only the four waves of rows
-  // 0..127 compute). Wave 0 counts both kinds per expert (inclusive prefixes over the
+  // one half tile (its last, of at most 128 rows, about two thirds the cost of a full
+  // one). Wave 0 counts both kinds per expert (inclusive prefixes over the
   // experts, 64 a round, kept in registers). The grid is sized from a bound; the real
   // tiles are dealt to the 8 XCDs (workgroup ids go round-robin to them), each kind in
   // equal contiguous runs with N fastest: XCD x runs its share of the full tiles, then
@@ -240,10 +240,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   uint32_t rs[2];
   // Part q of step st's global loads into set S: activation row q of this thread and,
   // for q = 3, the weight unit (whose four store parts have then all been written).
-  auto load_part = [&](auto SET, int st, int q) {
+  // (lo_only: a half tile, whose activation rows 128..255 are not needed)
+  auto load_part = [&](auto SET, int st, int q, bool lo_only) {
     constexpr int S = decltype(SET)::value;
     const int k0 = st * BK;
-    ra[S][q] = *reinterpret_cast<const u32x4*>(a_src[q] + k0);
+    if (q < 2 || !lo_only) ra[S][q] = *reinterpret_cast<const u32x4*>(a_src[q] + k0);
     if (q == 3) {
       const size_t toff = (size_t)(st >> 1) * 1024 + (st & 1) * 512;
       const size_t soff = (size_t)(st >> 1) * 128 + (st & 1) * 64;
@@ -253,9 +254,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   };
   // Part q (0..3) of writing set S into LDS buffer `buf`: activation row q of this
   // thread, and BF16 chunk q of the weight unit (dequantised here).
-  auto store_part = [&](auto SET, int buf, int q) {
+  auto store_part = [&](auto SET, int buf, int q, bool lo_only) {
     constexpr int S = decltype(SET)::value;
-    *reinterpret_cast<u32x4*>(&lds_a[buf][a_st + 64 * q * BK]) = ra[S][q];
+    if (q < 2 || !lo_only) *reinterpret_cast<u32x4*>(&lds_a[buf][a_st + 64 * q * BK]) = ra[S][q];
     const float sc = q < 2 ? e4m3_to_f32<0>(rs[S]) : e4m3_to_f32<1>(rs[S]);
     *reinterpret_cast<u32x4*>(&lds_b[buf][b_st[0] * BK + (((4 * b_kq + q) ^ b_sw) << 3)]) = dequant8(rb[S][q], sc);
   };
@@ -263,6 +264,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   using S1 = std::integral_constant<int, 1>;
 
   // ---- per-wave tile: 128 rows x 64 LDS B rows as 4 x 2 blocks of 32x32x16 MFMAs ----
+  // An expert's last tile of at most 128 rows (a half tile) is computed by all eight
+  // waves as 64-row x 64 tiles (2 x 2 blocks), two waves per SIMD as in a full tile;
+  // the activation rows 128..255 of such a tile are neither loaded nor stored.
   const int wm = wave >> 2, wn = wave & 3;
   const int r32 = lane & 31, kh = lane >> 5;  // operand row within a 32-block; K half (8 values)
   // LDS B rows of block j: up = gate rows 64wn + 32j (j < 2) then up rows
@@ -271,121 +275,110 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) boff[j] = kUp ? 128 * j + 32 * wn : 64 * wn + 32 * j;
   const int f_sw = swz_key(r32);
-  const int fa_base = (128 * wm + r32) * BK, fb_base = r32 * BK;
+  const int fb_base = r32 * BK;
 
-  f32x16 acc[4][2];
+  auto compute = [&](auto HALF) {
+    constexpr bool kHalf = decltype(HALF)::value;
+    // Prologue: step 0 into LDS buffer 0, steps 1 and 2 into register sets 1 and 0.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 4; ++q) load_part(S0{}, 0, q, kHalf);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int q = 0; q < 4; ++q) store_part(S0{}, 0, q, kHalf);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int q = 0; q < 4; ++q) load_part(S1{}, min(1, nsteps - 1), q, kHalf);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_part(S0{}, min(2, nsteps - 1), q, kHalf);
+    __syncthreads();
+    constexpr int MI = kHalf ? 2 : 4;  // 32-row blocks of a wave's tile
+    constexpr int WR = 32 * MI;        // rows of a wave's tile
+    const int fa_base = (WR * wm + r32) * BK;
+    f32x16 acc[MI][2];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // operand fragments of one 16-wide K substep
-  u32x4 fa[4], fb[2], na[4], nb[2];
-  auto read_frags = [&](int buf, int ks, u32x4* A, u32x4* Bv) {
-    const int cs = ((2 * ks + kh) ^ f_sw) << 3;
+    // operand fragments of one 16-wide K substep
+    u32x4 fa[MI], fb[2], na[MI], nb[2];
+    auto read_frags = [&](int buf, int ks, u32x4* A, u32x4* Bv) {
+      const int cs = ((2 * ks + kh) ^ f_sw) << 3;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) Bv[j] = *reinterpret_cast<const u32x4*>(&lds_b[buf][fb_base + boff[j] * BK + cs]);
+      for (int j = 0; j < 2; ++j) Bv[j] = *reinterpret_cast<const u32x4*>(&lds_b[buf][fb_base + boff[j] * BK + cs]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const u32x4*>(&lds_a[buf][fa_base + 32 * i * BK + cs]);
-  };
-
-  // Prologue: step 0 into LDS buffer 0, steps 1 and 2 into register sets 1 and 0.
-#pragma unroll
-  for (int q = 0; q < 4; ++q) load_part(S0{}, 0, q);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) store_part(S0{}, 0, q);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) load_part(S1{}, min(1, nsteps - 1), q);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) load_part(S0{}, min(2, nsteps - 1), q);
-  __syncthreads();
-  // A tile of at most 128 rows (an expert's last, partial tile) leaves the waves of the
-  // lower half (wm = 1) without rows: they only copy their share of every step into LDS.
-  // Steps come in pairs (K is a multiple of 128): step st writes set (st + 1) % 2.
-  if (rows <= 128 && wm == 1) {
-    auto copy_step = [&](auto SET, int st) {
+      for (int i = 0; i < MI; ++i) A[i] = *reinterpret_cast<const u32x4*>(&lds_a[buf][fa_base + 32 * i * BK + cs]);
+    };
+    read_frags(0, 0, fa, fb);
+    // Steps come in pairs (K is a multiple of 128): step st writes set (st + 1) % 2.
+    auto step = [&](auto SET, int st) {
+      const int buf = st & 1;
+      const int next3 = min(st + 3, nsteps - 1);  // the last steps reload themselves (never read)
+      // Four 16-wide substeps. In each, the next substep's fragments are read while this
+      // one's MFMAs run; then one part of step st+1 is written to the other buffer, and
+      // its registers are refilled with step st+3.
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
-        store_part(SET, (st & 1) ^ 1, ks);
-        load_part(SET, min(st + 3, nsteps - 1), ks);
+        if (ks + 1 < BK / 16) read_frags(buf, ks + 1, na, nb);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+        store_part(SET, buf ^ 1, ks, kHalf);
+        load_part(SET, next3, ks, kHalf);
+        if (ks + 1 < BK / 16) {
+#pragma unroll
+          for (int i = 0; i < MI; ++i) fa[i] = na[i];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) fb[j] = nb[j];
+        }
       }
       __syncthreads();
+      read_frags(buf ^ 1, 0, fa, fb);
     };
     for (int st = 0; st < nsteps; st += 2) {
-      copy_step(S1{}, st);
-      copy_step(S0{}, st + 1);
+      step(S1{}, st);
+      step(S0{}, st + 1);
     }
-    __syncthreads();  // the epilogue's barrier
-    return;
-  }
-  read_frags(0, 0, fa, fb);
-  auto step = [&](auto SET, int st) {
-    const int buf = st & 1;
-    const int next3 = min(st + 3, nsteps - 1);  // the last steps reload themselves (never read)
-    // Four 16-wide substeps. In each, the next substep's fragments are read while this
-    // one's MFMAs run; then one part of step st+1 is written to the other buffer, and
-    // its registers are refilled with step st+3.
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) read_frags(buf, ks + 1, na, nb);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
-      store_part(SET, buf ^ 1, ks);
-      load_part(SET, next3, ks);
-      if (ks + 1 < BK / 16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = na[i];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) fb[j] = nb[j];
-      }
-    }
-    __syncthreads();
-    read_frags(buf ^ 1, 0, fa, fb);
-  };
-  for (int st = 0; st < nsteps; st += 2) {
-    step(S1{}, st);
-    step(S0{}, st + 1);
-  }
 
-  // ---- epilogue: acc[i][j][r] is row 8(r/4) + 4kh + r%4, column r32 of block (i, j) ----
-  // The wave's outputs go through LDS (the operand buffers are free once every wave has
-  // passed the barrier), so that each lane writes whole 16-byte row pieces: 8 (up) or 16
-  // (down) stores a wave instead of 64 or 128 of 2 bytes. A wave's LDS region is its own
-  // [128][W] BF16 block (W = 32 h columns for up, 64 y columns for down).
-  __syncthreads();
-  constexpr int W = kUp ? 32 : 64;
-  uint16_t* stage = (wave < 4 ? &lds_a[0][0] : &lds_b[0][0]) + (wave & 3) * (128 * W);
+    // ---- epilogue: acc[i][j][r] is row 8(r/4) + 4kh + r%4, column r32 of block (i, j) ----
+    // The wave's outputs go through LDS (the operand buffers are free once every wave
+    // has passed the barrier), so that each lane writes whole 16-byte row pieces: 8 (up)
+    // or 16 (down) stores a wave instead of 64 or 128 of 2 bytes. A wave's LDS region is
+    // its own [WR][W] BF16 block (W = 32 h columns for up, 64 y columns for down).
+    __syncthreads();
+    constexpr int W = kUp ? 32 : 64;
+    uint16_t* stage = (wave < 4 ? &lds_a[0][0] : &lds_b[0][0]) + (wave & 3) * (128 * W);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lr = 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
-      if (kUp) {
-        stage[lr * W + r32] = f32_to_bf16(silu_mul(ts * acc[i][0][r], ts * acc[i][1][r]));
-      } else {
+      for (int r = 0; r < 16; ++r) {
+        const int lr = 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (kUp) {
+          stage[lr * W + r32] = f32_to_bf16(silu_mul(ts * acc[i][0][r], ts * acc[i][1][r]));
+        } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) stage[lr * W + 32 * j + r32] = f32_to_bf16(ts * acc[i][j][r]);
+          for (int j = 0; j < 2; ++j) stage[lr * W + 32 * j + r32] = f32_to_bf16(ts * acc[i][j][r]);
+        }
       }
     }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  constexpr int kPieces = 128 * W / 8;  // 16-byte pieces of the wave's block
-  const size_t ld = kUp ? a.I : a.N;
-  const int col0 = kUp ? nt * 128 + 32 * wn : nt * BN + 64 * wn;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int kPieces = WR * W / 8;  // 16-byte pieces of the wave's block
+    const size_t ld = kUp ? a.I : a.N;
+    const int col0 = kUp ? nt * 128 + 32 * wn : nt * BN + 64 * wn;
 #pragma unroll
-  for (int c = 0; c < kPieces / 64; ++c) {
-    const int piece = 64 * c + lane, lr = piece / (W / 8), lc = (piece % (W / 8)) * 8;
-    const int tr = 128 * wm + lr;
-    if (tr < rows)
-      *reinterpret_cast<u32x4*>(a.out + (size_t)(row0 + tr) * ld + col0 + lc) =
-          *reinterpret_cast<const u32x4*>(stage + lr * W + lc);
-  }
+    for (int c = 0; c < kPieces / 64; ++c) {
+      const int piece = 64 * c + lane, lr = piece / (W / 8), lc = (piece % (W / 8)) * 8;
+      const int tr = WR * wm + lr;
+      if (tr < rows)
+        *reinterpret_cast<u32x4*>(a.out + (size_t)(row0 + tr) * ld + col0 + lc) =
+            *reinterpret_cast<const u32x4*>(stage + lr * W + lc);
+    }
+  };
+  if (rows <= 128) compute(std::true_type{});
+  else compute(std::false_type{});
 }
 
 hipError_t launch(bool up, GemmArgs a, long long m_tiles, hipStream_t s) {

@@ -205,6 +205,21 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   // consecutive pairs (of one expert: pairs_per_group is a multiple of 4)
   const int b = blockIdx.x, C = a.slots;
   const int unit = kPerExpert ? b * groups + gi : ((b / C) * groups + gi) * C + (b % C);
+  // All-rows form: the first round of the activation copy (8 chunks of 16 bytes per
+  // thread) depends on nothing, so it goes out before the expert lookup and the weight
+  // tiles. Loads return in issue order; issued after the tiles, the copy would wait
+  // for them, and the workgroup's barrier with it.
+  constexpr int kU = 8;
+  u32x4 pre[kX == kXAll ? kU : 1];
+  if constexpr (kX == kXAll) {
+    const int cpr = K / 8, total = a.stage_rows * cpr;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = u * 256 + tid;
+      const int cc = c < total ? c : 0;
+      pre[u] = reinterpret_cast<const u32x4*>(a.act + (size_t)(cc / cpr) * K)[cc % cpr];
+    }
+  }
   const Group grp = find_group(a, unit / pairs_per_group);
   const int g = grp.g, r0 = grp.r0, M = grp.M;
   const int pair = unit % pairs_per_group;
@@ -277,7 +292,13 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
     const int cpr = kc / 8;  // 16-byte chunks per row
     const int total = nrows * cpr;
     // 8 chunks per thread: all loads, then all stores
-    constexpr int kU = 8;
+    auto store8 = [&](int base, const u32x4* buf) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int c = base + u * 256 + tid;
+        if (c < total) *reinterpret_cast<u32x4*>(smem + (size_t)(c / cpr) * xs + (c % cpr) * 16) = buf[u];
+      }
+    };
     auto copy8 = [&](int base) {
       u32x4 buf[kU];
 #pragma unroll
@@ -286,11 +307,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
         const int cc = c < total ? c : 0;
         buf[u] = reinterpret_cast<const u32x4*>(a.act + (size_t)srcrow(cc / cpr) * K + k0)[cc % cpr];
       }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int c = base + u * 256 + tid;
-        if (c < total) *reinterpret_cast<u32x4*>(smem + (size_t)(c / cpr) * xs + (c % cpr) * 16) = buf[u];
-      }
+      store8(base, buf);
     };
     if constexpr (kSlice) {
       // straight into LDS, every load of the slice in flight at once: a wave moves 1 KB
@@ -307,8 +324,15 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
     } else {
       // the first round outside the loop: a loop head would wait for every load in
       // flight (the weight tiles issued before included) before reusing its registers
-      copy8(0);
-      for (int base = kU * 256; base < total; base += kU * 256) copy8(base);
+      int base = 0;
+      if constexpr (kX == kXAll) {  // the first round was loaded at the start
+        store8(0, pre);
+        base = kU * 256;
+      } else {
+        copy8(0);
+        base = kU * 256;
+      }
+      for (; base < total; base += kU * 256) copy8(base);
     }
     __syncthreads();
     for (int row = wave; row < nrows; row += 4) {  // wave w converts rows w, w+4, ...

@@ -28,7 +28,6 @@
 // rows are laid out, and each wave finds its expert among the non-empty ones from the
 // offsets.
 #include <algorithm>
-#include <type_traits>
 
 #include "device.hpp"
 #include "launch.hpp"
@@ -211,9 +210,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   // tiles. Loads return in issue order; issued after the tiles, the copy would wait
   // for them, and the workgroup's barrier with it.
   constexpr int kU = 8;
-  constexpr bool kPreExpert = kX == kXExpert && !kUp;  // down: the expert's rows are contiguous
-  constexpr int kUPre = kX == kXAll ? kU : 1;  // rounds loaded early
-  u32x4 pre[kUPre];
+  u32x4 pre[kX == kXAll ? kU : 1];
   if constexpr (kX == kXAll) {
     const int cpr = K / 8, total = a.stage_rows * cpr;
 #pragma unroll
@@ -226,17 +223,6 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   const Group grp = find_group(a, unit / pairs_per_group);
   const int g = grp.g, r0 = grp.r0, M = grp.M;
   const int pair = unit % pairs_per_group;
-  // Down, expert form: pass 0's rows r0 .. r0 + min(M, rows) - 1 are contiguous and
-  // known once the expert is, so their first copy round goes out before the tiles too.
-  if constexpr (kPreExpert) {
-    const int cpr = K / 8, total = min(M, a.stage_rows) * cpr;
-#pragma unroll
-    for (int u = 0; u < kUPre; ++u) {
-      const int c = u * 256 + tid;
-      const int cc = c < total ? c : 0;
-      pre[u] = reinterpret_cast<const u32x4*>(a.act + (size_t)(r0 + cc / cpr) * K)[cc % cpr];
-    }
-  }
   // rows per pass: an MFMA's 16, or the staged rows of the expert form
   const int rows_pass = kPerExpert ? a.stage_rows : 16;
   const int npass = (M + rows_pass - 1) / rows_pass;
@@ -302,13 +288,13 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   // copy columns [k0, k0 + kc) of act rows srcrow(i), i < nrows, into LDS rows i, then
   // convert them in place to FP16, each scaled by 2^-sh so that its max |x| is below
   // 2^15, keeping 2^sh in row_scale (the caller synchronises before and after)
-  auto stage_rows = [&](int nrows, auto srcrow, int k0, int kc, auto from_pre) {
+  auto stage_rows = [&](int nrows, auto srcrow, int k0, int kc) {
     const int cpr = kc / 8;  // 16-byte chunks per row
     const int total = nrows * cpr;
     // 8 chunks per thread: all loads, then all stores
-    auto store8 = [&](int base, const u32x4* buf, int n) {
+    auto store8 = [&](int base, const u32x4* buf) {
 #pragma unroll
-      for (int u = 0; u < n; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const int c = base + u * 256 + tid;
         if (c < total) *reinterpret_cast<u32x4*>(smem + (size_t)(c / cpr) * xs + (c % cpr) * 16) = buf[u];
       }
@@ -321,7 +307,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
         const int cc = c < total ? c : 0;
         buf[u] = reinterpret_cast<const u32x4*>(a.act + (size_t)srcrow(cc / cpr) * K + k0)[cc % cpr];
       }
-      store8(base, buf, kU);
+      store8(base, buf);
     };
     if constexpr (kSlice) {
       // straight into LDS, every load of the slice in flight at once: a wave moves 1 KB
@@ -339,9 +325,9 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
       // the first round outside the loop: a loop head would wait for every load in
       // flight (the weight tiles issued before included) before reusing its registers
       int base = 0;
-      if constexpr (decltype(from_pre)::value) {  // the first round was loaded at the start
-        if constexpr (kX == kXAll) store8(0, pre, kUPre);  // (the expert form stored it already)
-        base = kUPre * 256;
+      if constexpr (kX == kXAll) {  // the first round was loaded at the start
+        store8(0, pre);
+        base = kU * 256;
       } else {
         copy8(0);
         base = kU * 256;
@@ -383,21 +369,13 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) issue(st[i], s_begin + i);
   }
-  if constexpr (kPreExpert) {  // pass 0's early round into LDS, so `pre` is dead in the loop
-    const int cpr = K / 8, total = min(M, a.stage_rows) * cpr, xs0 = x_row_stride(K);
-#pragma unroll
-    for (int u = 0; u < kUPre; ++u) {
-      const int c = u * 256 + tid;
-      if (c < total) *reinterpret_cast<u32x4*>(smem + (size_t)(c / cpr) * xs0 + (c % cpr) * 16) = pre[u];
-    }
-  }
   // passes of the workgroup: the most of its groups (the K-split hand-over and the
   // expert form's copies are workgroup barriers, so every wave runs as many passes)
   if (tid == 0) s_npass = 0;
   __syncthreads();
   if (lane == 0 && q == 0 && npass > 0) atomicMax(&s_npass, npass);
   if constexpr (kX == kXAll) {
-    stage_rows(a.stage_rows, [&](int i) { return i; }, 0, K, std::true_type{});
+    stage_rows(a.stage_rows, [&](int i) { return i; }, 0, K);
     __syncthreads();
   }
   __syncthreads();
@@ -414,13 +392,12 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
         __syncthreads();  // the previous pass's reads are done
         pair0 = row_pair(pass);
       }
-      if (kPreExpert && pass == 0) stage_rows(nr, [&](int i) { return row_src(__shfl(pair0, i)); }, 0, K, std::true_type{});
-      else stage_rows(nr, [&](int i) { return row_src(__shfl(pair0, i)); }, 0, K, std::false_type{});
+      stage_rows(nr, [&](int i) { return row_src(__shfl(pair0, i)); }, 0, K);
       __syncthreads();
     }
     // the expert's rows of this pass, K slice `slc` (the caller synchronises before)
     auto stage_slice = [&](int slc) {
-      stage_rows(nr, [&](int i) { return row_src(__shfl(pair0, i)); }, slc * (K / kSlices), K / kSlices, std::false_type{});
+      stage_rows(nr, [&](int i) { return row_src(__shfl(pair0, i)); }, slc * (K / kSlices), K / kSlices);
       __syncthreads();
     };
     if constexpr (kSlice) {
@@ -598,13 +575,12 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
     mode = kXSlice;  // a slice's steps are whole rounds of the ring
     stage_rows = rows_alloc;
   }
-  // The down projection of a small batch (9 to 64 routed rows, e.g. decode T*k = 64)
-  // reads its few h rows straight from the cache: staging them costs each workgroup a
-  // copy and a conversion (a chain of barriers) before its first MFMA, more than the
-  // BF16 form's extra dequantisation (measured: 15.6 against 20.2 us at T = 8, k = 8).
-  // With 8 rows or fewer the staged expert form wins (10.7 against 11.9 us at T = 1):
-  // its first copy round goes out before the weight tiles. Up is faster staged.
-  if (!up && all_rows > 8 && all_rows <= 64) {
+  // The down projection of a small batch (at most 64 routed rows, i.e. decode up to
+  // T*k = 64) reads its few h rows straight from the cache: staging them costs each
+  // workgroup a copy and a conversion (a chain of barriers) before its first MFMA, more
+  // than the BF16 form's extra dequantisation (measured: -1.9 us per layer at T = 1,
+  // -1.1 us at T = 8; up is faster staged).
+  if (!up && all_rows <= 64) {
     mode = kXRegs;
     stage_rows = 0;
   }

@@ -16,8 +16,9 @@
 // 128 x 128 per SIMD the same tile ran slower). For the up projection the 256 weight
 // rows are 128 gate rows and the matching 128 up rows, and each wave takes 32 of each,
 // so gate and up accumulators of the same h columns sit in the same lanes and SwiGLU
-// is applied in registers. An expert's last tile, when it has at most 128 rows, is
-// computed by all eight waves as 64 x 64 tiles, again two waves per SIMD.
+// is applied in registers. An expert's last tile, when it has at most 192 (or 128)
+// rows, is computed by all eight waves as 96 x 64 (or 64 x 64) tiles, again two waves
+// per SIMD, and the activation rows past 192 (or 128) are neither loaded nor stored.
 //
 // Pipeline. Activation rows (gathered through perm_src for the up projection) and
 // weight half-tiles (tiled layout, 512 contiguous bytes per 16-row block) are loaded
@@ -47,6 +48,7 @@ namespace moe4 {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kTq = 192;  // rows of a three-quarter tile
 constexpr int kThreads = 512;
 constexpr int kXcds = 8;
 constexpr int kMaxExperts = 256;  // the ABI's bound on G
@@ -84,13 +86,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // Tile schedule. An expert's M-tiles are full tiles (more than 128 rows) and at most
-  // one half tile (its last, of at most 128 rows, about two thirds the cost of a full
-  // one). Wave 0 counts both kinds per expert (inclusive prefixes over the
-  // experts, 64 a round, kept in registers). The grid is sized from a bound; the real
-  // tiles are dealt to the 8 XCDs (workgroup ids go round-robin to them), each kind in
-  // equal contiguous runs with N fastest: XCD x runs its share of the full tiles, then
-  // its share of the half tiles. So the workgroups sharing an activation tile, and an
+  // Tile schedule. An expert's M-tiles are full tiles (more than 192 rows) and at most
+  // one shorter last tile: three-quarter (129 to 192 rows) or half (at most 128 rows,
+  // about two thirds the cost of a full one). Wave 0 counts the three kinds per expert
+  // (inclusive prefixes over the experts, 64 a round, kept in registers). The grid is
+  // sized from a bound; the real tiles are dealt to the 8 XCDs (workgroup ids go
+  // round-robin to them), each kind in equal contiguous runs with N fastest: XCD x runs
+  // its share of the full tiles, then of the three-quarter ones, then of the half ones.
+  // So the workgroups sharing an activation tile, and an
   // expert's weights, meet in the same L2, every XCD gets the same amount of work
   // whatever the routing, and each XCD ends on short tiles. Workgroups past their XCD's
   // runs exit at once. (Dealing the bound's range in one run left the last XCDs with
@@ -99,59 +102,80 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   if (wave == 0) {
     int g = -1, r0 = 0, rows = 0, nt = 0;
     const int j = blockIdx.x / kXcds, x = blockIdx.x % kXcds;
+    // tiles of each class for an expert of cnt rows
+    auto classes = [](int cnt, int& f, int& t, int& h) {
+      const int rem = cnt % BM;
+      f = cnt / BM + (rem > kTq ? 1 : 0);
+      t = rem > BM / 2 && rem <= kTq ? 1 : 0;
+      h = rem != 0 && rem <= BM / 2 ? 1 : 0;
+    };
+    // this workgroup's place in its XCD's runs: class (0 full, 1 three-quarter, 2 half)
+    // and the index of its tile within the class, or q = -1
+    auto place = [&](int n_f, int n_t, int n_h, int& q, int& cls) {
+      const int per_f = (n_f + kXcds - 1) / kXcds, per_t = (n_t + kXcds - 1) / kXcds;
+      const int per_h = (n_h + kXcds - 1) / kXcds;
+      q = -1;
+      cls = 0;
+      if (j < per_f) {
+        q = x * per_f + j;
+        if (q >= n_f) q = -1;
+      } else if (j - per_f < per_t) {
+        q = x * per_t + (j - per_f);
+        cls = 1;
+        if (q >= n_t) q = -1;
+      } else if (j - per_f - per_t < per_h) {
+        q = x * per_h + (j - per_f - per_t);
+        cls = 2;
+        if (q >= n_h) q = -1;
+      }
+    };
     if (a.offsets) {
-      int incl_f[kMaxExperts / 64], incl_h[kMaxExperts / 64];
-      int carry_f = 0, carry_h = 0;
+      int incl_f[kMaxExperts / 64], incl_t[kMaxExperts / 64], incl_h[kMaxExperts / 64];
+      int carry_f = 0, carry_t = 0, carry_h = 0;
 #pragma unroll
       for (int c = 0; c < kMaxExperts / 64; ++c) {
         const int e = 64 * c + lane;
         const int cnt = e < a.G ? a.offsets[e + 1] - a.offsets[e] : 0;
-        int f = cnt / BM + (cnt % BM > BM / 2 ? 1 : 0);
-        int h = (cnt % BM != 0 && cnt % BM <= BM / 2) ? 1 : 0;
+        int f, t, h;
+        classes(cnt, f, t, h);
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-          const int of = __shfl_up(f, off), oh = __shfl_up(h, off);
+          const int of = __shfl_up(f, off), ot = __shfl_up(t, off), oh = __shfl_up(h, off);
           if (lane >= off) {
             f += of;
+            t += ot;
             h += oh;
           }
         }
         incl_f[c] = carry_f + f;
+        incl_t[c] = carry_t + t;
         incl_h[c] = carry_h + h;
         carry_f += __shfl(f, 63);
+        carry_t += __shfl(t, 63);
         carry_h += __shfl(h, 63);
       }
-      const int n_f = carry_f * a.n_tiles, n_h = carry_h * a.n_tiles;
-      const int per_f = (n_f + kXcds - 1) / kXcds, per_h = (n_h + kXcds - 1) / kXcds;
-      // this workgroup's tile: class (full / half), index of the M-tile within the class
-      int q = -1, half = 0;
-      if (j < per_f) {
-        q = x * per_f + j;
-        if (q >= n_f) q = -1;
-      } else if (j - per_f < per_h) {
-        q = x * per_h + (j - per_f);
-        half = 1;
-        if (q >= n_h) q = -1;
-      }
+      int q, cls;
+      place(carry_f * a.n_tiles, carry_t * a.n_tiles, carry_h * a.n_tiles, q, cls);
       if (q >= 0) {
         const int m = q / a.n_tiles;
         nt = q % a.n_tiles;
+        auto incl_of = [&](int c) { return cls == 0 ? incl_f[c] : (cls == 1 ? incl_t[c] : incl_h[c]); };
 #pragma unroll
         for (int c = 0; c < kMaxExperts / 64; ++c) {
           const int e = 64 * c + lane;
-          const int incl = half ? incl_h[c] : incl_f[c];
+          const int incl = incl_of(c);
           const int prev = __shfl_up(incl, 1);  // every lane takes part in both shuffles
-          const int before = c == 0 ? 0 : __shfl(half ? incl_h[c > 0 ? c - 1 : 0] : incl_f[c > 0 ? c - 1 : 0], 63);
+          const int before = c == 0 ? 0 : __shfl(incl_of(c > 0 ? c - 1 : 0), 63);
           const int excl = lane == 0 ? before : prev;
           const uint64_t hit = __ballot(e < a.G && m >= excl && m < incl);
           if (hit && g < 0) {
             const int src = __ffsll((long long)hit) - 1;
             g = __shfl(e, src);
-            const int mt = half ? 0 : m - __shfl(excl, src);
+            const int mt = cls ? 0 : m - __shfl(excl, src);
             r0 = a.offsets[g];
             const int cnt = a.offsets[g + 1] - r0;
-            // a half tile is the expert's last M-tile
-            const int m0 = half ? cnt / BM : mt;
+            // a three-quarter or half tile is the expert's last M-tile
+            const int m0 = cls ? cnt / BM : mt;
             r0 += m0 * BM;
             rows = min(BM, cnt - m0 * BM);
           }
@@ -160,22 +184,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
     } else {
       // dense: one group of T rows
       const int cnt = a.T;
-      const int n_f = (cnt / BM + (cnt % BM > BM / 2 ? 1 : 0)) * a.n_tiles;
-      const int n_h = ((cnt % BM != 0 && cnt % BM <= BM / 2) ? 1 : 0) * a.n_tiles;
-      const int per_f = (n_f + kXcds - 1) / kXcds, per_h = (n_h + kXcds - 1) / kXcds;
-      int q = -1, half = 0;
-      if (j < per_f) {
-        q = x * per_f + j;
-        if (q >= n_f) q = -1;
-      } else if (j - per_f < per_h) {
-        q = x * per_h + (j - per_f);
-        half = 1;
-        if (q >= n_h) q = -1;
-      }
+      int f, t, h, q, cls;
+      classes(cnt, f, t, h);
+      place(f * a.n_tiles, t * a.n_tiles, h * a.n_tiles, q, cls);
       if (q >= 0) {
         g = 0;
         nt = q % a.n_tiles;
-        const int m0 = half ? cnt / BM : q / a.n_tiles;
+        const int m0 = cls ? cnt / BM : q / a.n_tiles;
         r0 = m0 * BM;
         rows = min(BM, cnt - m0 * BM);
       }
@@ -240,11 +255,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   uint32_t rs[2];
   // Part q of step st's global loads into set S: activation row q of this thread and,
   // for q = 3, the weight unit (whose four store parts have then all been written).
-  // (lo_only: a half tile, whose activation rows 128..255 are not needed)
-  auto load_part = [&](auto SET, int st, int q, bool lo_only) {
+  // (groups: the activation row groups of 64 the tile needs, 4, 3 or 2)
+  auto load_part = [&](auto SET, int st, int q, int groups) {
     constexpr int S = decltype(SET)::value;
     const int k0 = st * BK;
-    if (q < 2 || !lo_only) ra[S][q] = *reinterpret_cast<const u32x4*>(a_src[q] + k0);
+    if (q < groups) ra[S][q] = *reinterpret_cast<const u32x4*>(a_src[q] + k0);
     if (q == 3) {
       const size_t toff = (size_t)(st >> 1) * 1024 + (st & 1) * 512;
       const size_t soff = (size_t)(st >> 1) * 128 + (st & 1) * 64;
@@ -254,9 +269,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   };
   // Part q (0..3) of writing set S into LDS buffer `buf`: activation row q of this
   // thread, and BF16 chunk q of the weight unit (dequantised here).
-  auto store_part = [&](auto SET, int buf, int q, bool lo_only) {
+  auto store_part = [&](auto SET, int buf, int q, int groups) {
     constexpr int S = decltype(SET)::value;
-    if (q < 2 || !lo_only) *reinterpret_cast<u32x4*>(&lds_a[buf][a_st + 64 * q * BK]) = ra[S][q];
+    if (q < groups) *reinterpret_cast<u32x4*>(&lds_a[buf][a_st + 64 * q * BK]) = ra[S][q];
     const float sc = q < 2 ? e4m3_to_f32<0>(rs[S]) : e4m3_to_f32<1>(rs[S]);
     *reinterpret_cast<u32x4*>(&lds_b[buf][b_st[0] * BK + (((4 * b_kq + q) ^ b_sw) << 3)]) = dequant8(rb[S][q], sc);
   };
@@ -264,9 +279,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   using S1 = std::integral_constant<int, 1>;
 
   // ---- per-wave tile: 128 rows x 64 LDS B rows as 4 x 2 blocks of 32x32x16 MFMAs ----
-  // An expert's last tile of at most 128 rows (a half tile) is computed by all eight
-  // waves as 64-row x 64 tiles (2 x 2 blocks), two waves per SIMD as in a full tile;
-  // the activation rows 128..255 of such a tile are neither loaded nor stored.
+  // An expert's last tile of at most 192 rows (three-quarter) or 128 rows (half) is
+  // computed by all eight waves as 96- or 64-row x 64 tiles (3 x 2 or 2 x 2 blocks),
+  // two waves per SIMD as in a full tile; the activation rows past 192 or 128 are
+  // neither loaded nor stored. Each output is the same chain of MFMAs over K in every
+  // tile shape, so the shape does not change any bits.
   const int wm = wave >> 2, wn = wave & 3;
   const int r32 = lane & 31, kh = lane >> 5;  // operand row within a 32-block; K half (8 values)
   // LDS B rows of block j: up = gate rows 64wn + 32j (j < 2) then up rows
@@ -277,19 +294,18 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   const int f_sw = swz_key(r32);
   const int fb_base = r32 * BK;
 
-  auto compute = [&](auto HALF) {
-    constexpr bool kHalf = decltype(HALF)::value;
+  auto compute = [&](auto MIC) {
+    constexpr int MI = decltype(MIC)::value;  // 32-row blocks of a wave's tile: 4, 3 or 2
     // Prologue: step 0 into LDS buffer 0, steps 1 and 2 into register sets 1 and 0.
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load_part(S0{}, 0, q, kHalf);
+    for (int q = 0; q < 4; ++q) load_part(S0{}, 0, q, MI);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) store_part(S0{}, 0, q, kHalf);
+    for (int q = 0; q < 4; ++q) store_part(S0{}, 0, q, MI);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load_part(S1{}, min(1, nsteps - 1), q, kHalf);
+    for (int q = 0; q < 4; ++q) load_part(S1{}, min(1, nsteps - 1), q, MI);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load_part(S0{}, min(2, nsteps - 1), q, kHalf);
+    for (int q = 0; q < 4; ++q) load_part(S0{}, min(2, nsteps - 1), q, MI);
     __syncthreads();
-    constexpr int MI = kHalf ? 2 : 4;  // 32-row blocks of a wave's tile
     constexpr int WR = 32 * MI;        // rows of a wave's tile
     const int fa_base = (WR * wm + r32) * BK;
     f32x16 acc[MI][2];
@@ -324,8 +340,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
-        store_part(SET, buf ^ 1, ks, kHalf);
-        load_part(SET, next3, ks, kHalf);
+        store_part(SET, buf ^ 1, ks, MI);
+        load_part(SET, next3, ks, MI);
         if (ks + 1 < BK / 16) {
 #pragma unroll
           for (int i = 0; i < MI; ++i) fa[i] = na[i];
@@ -377,15 +393,16 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
             *reinterpret_cast<const u32x4*>(stage + lr * W + lc);
     }
   };
-  if (rows <= 128) compute(std::true_type{});
-  else compute(std::false_type{});
+  if (rows <= BM / 2) compute(std::integral_constant<int, 2>{});
+  else if (rows <= kTq) compute(std::integral_constant<int, 3>{});
+  else compute(std::integral_constant<int, 4>{});
 }
 
 hipError_t launch(bool up, GemmArgs a, long long m_tiles, hipStream_t s) {
   a.n_tiles = up ? a.I / 128 : a.N / BN;
   const long long tiles = m_tiles * a.n_tiles;
-  // each of the two runs of an XCD (full tiles, half tiles) may round up by one
-  a.total = (int)((tiles + kXcds - 1) / kXcds * kXcds) + 2 * kXcds;
+  // each of the three runs of an XCD (full, three-quarter, half tiles) may round up by one
+  a.total = (int)((tiles + kXcds - 1) / kXcds * kXcds) + 3 * kXcds;
   if (up) hipLaunchKernelGGL(ffn_prefill_kernel<true>, dim3(a.total), dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(ffn_prefill_kernel<false>, dim3(a.total), dim3(kThreads), 0, s, a);
   return hipGetLastError();

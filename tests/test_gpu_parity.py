@@ -279,10 +279,11 @@ def test_expert_ffn_routed(name, w, _):
 
 
 def test_expert_ffn_tile_edges():
-    """Expert groups on the prefill GEMM's tile boundaries: 128 rows (a half-height
-    tile), 129 (a full tile with one row in its lower half), 256, 257, 384 (a full tile
-    and a half one) and 1 row."""
-    counts = [128, 129, 256, 257, 384, 1]
+    """Expert groups on the prefill GEMM's tile boundaries: 128 rows (a half tile), 129
+    and 192 (three-quarter tiles), 193 (a full tile with one row in its last quarter),
+    256, 257, 384 (a full tile and a half one), 416 (a full and a three-quarter one)
+    and 1 row."""
+    counts = [128, 129, 192, 193, 256, 257, 384, 416, 1]
     w = wl.Workload("tile_edges", T=sum(counts), H=512, E=len(counts), k=1, I=256, routing="normal")
     note(f"expert ffn tile edges: groups {counts}")
     inp = wl.make_inputs(w, seed=3)
@@ -295,11 +296,11 @@ def test_expert_ffn_tile_edges():
 def test_expert_ffn_prefill_schedule_edges():
     """The prefill GEMM's tile schedule over 256 experts, most of them empty: rows only
     at the ends of the 64-expert rounds of its per-expert count (experts 0, 63, 64, 127,
-    128, 191, 255), groups that give half tiles (1, 100 rows and a 109-row tail), padded
-    full tiles (129) and both (300, 385), and few tiles per XCD for the down GEMM (one N
-    tile)."""
+    128, 191, 255), groups that give half tiles (1, 100 rows and a 57-row tail),
+    three-quarter tiles (129, 170), padded full tiles (200) and tails of each kind after
+    full tiles (300, 385, 450), and few tiles per XCD for the down GEMM (one N tile)."""
     counts = np.zeros(256, dtype=np.int64)
-    for e, c in {0: 100, 63: 129, 64: 300, 127: 256, 128: 1, 191: 385}.items():
+    for e, c in {0: 100, 1: 170, 2: 200, 3: 450, 63: 129, 64: 300, 127: 256, 128: 1, 191: 385}.items():
         counts[e] = c
     T = 64 * 256  # k = 1: as many rows as the prefill kernel needs over 256 experts
     counts[255] = T - counts.sum()

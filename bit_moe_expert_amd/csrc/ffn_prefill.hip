@@ -131,11 +131,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
     };
     if (a.offsets) {
       int incl_f[kMaxExperts / 64], incl_t[kMaxExperts / 64], incl_h[kMaxExperts / 64];
+      int first[kMaxExperts / 64], count[kMaxExperts / 64];  // expert 64c + lane's rows
       int carry_f = 0, carry_t = 0, carry_h = 0;
 #pragma unroll
       for (int c = 0; c < kMaxExperts / 64; ++c) {
         const int e = 64 * c + lane;
-        const int cnt = e < a.G ? a.offsets[e + 1] - a.offsets[e] : 0;
+        first[c] = e < a.G ? a.offsets[e] : 0;
+        const int cnt = e < a.G ? a.offsets[e + 1] - first[c] : 0;
+        count[c] = cnt;
         int f, t, h;
         classes(cnt, f, t, h);
 #pragma unroll
@@ -172,8 +175,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
             const int src = __ffsll((long long)hit) - 1;
             g = __shfl(e, src);
             const int mt = cls ? 0 : m - __shfl(excl, src);
-            r0 = a.offsets[g];
-            const int cnt = a.offsets[g + 1] - r0;
+            r0 = __shfl(first[c], src);  // from the counting loads, not a second round trip
+            const int cnt = __shfl(count[c], src);
             // a three-quarter or half tile is the expert's last M-tile
             const int m0 = cls ? cnt / BM : mt;
             r0 += m0 * BM;

@@ -496,6 +496,10 @@ def test_layer_deterministic_and_batch_independent():
     d = g9.host()
     assert np.array_equal(d["idx"][:8], a["idx"])
     assert np.array_equal(d["o_bits"][:8], a["o_bits"]) and np.array_equal(d["n_bits"][:8], a["n_bits"])
+    # the ninth token repeats token 5; its activation row is staged by the up kernel's
+    # second copy round (9 rows of 2048 columns are 2304 16-byte chunks, 2048 a round)
+    assert np.array_equal(d["idx"][8], a["idx"][5])
+    assert np.array_equal(d["o_bits"][8], a["o_bits"][5]) and np.array_equal(d["n_bits"][8], a["n_bits"][5])
 
 
 # moe4_layer takes the fused top-k + plan launch for small batches and may pick other

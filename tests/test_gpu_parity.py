@@ -227,6 +227,9 @@ FFN_CASES = [
     ("expert_staged", wl.Workload("expert_staged", T=40, H=512, E=4, k=2, I=1024, routing="zipf"), None),
     # all rows staged once, many experts with rows
     ("all_staged", wl.Workload("all_staged", T=8, H=1024, E=256, k=8, I=1536, routing="normal"), None),
+    # few rows per expert on average (3), staged 8 rows a pass (16 do not fit LDS); the
+    # skewed routing gives some experts several passes
+    ("expert8_passes", wl.Workload("expert8_passes", T=48, H=2048, E=128, k=8, I=256, routing="zipf"), None),
     # activations in registers (neither all rows nor one expert's rows fit LDS), several passes
     ("regs_passes", wl.Workload("regs_passes", T=40, H=2048, E=4, k=2, I=256, routing="zipf"), None),
     # many rows per expert (the MFMA-tile kernel), ragged tails

@@ -563,8 +563,9 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
   // the activation source: all rows in LDS if they fit, else each expert's rows
   // (at most 16 per pass), else registers
   const int rows_alloc = (int)std::min<long long>(expert_rows, 16);
-  // routed rows per expert on average (all_rows counts tokens for up, routed rows for down)
-  const long long routed = up ? all_rows * a.k : all_rows;
+  // routed rows per expert on average (all_rows counts tokens for routed up, routed rows
+  // for down, the group's rows for a dense call)
+  const long long routed = up && a.offsets ? all_rows * a.k : all_rows;
   const long long avg_rows = a.offsets ? (routed + G - 1) / G : routed;
   int mode = kXRegs;
   int stage_rows = 0;

@@ -26,7 +26,11 @@ constexpr int kMaxE = 256;
 constexpr long long kSingleMax = 16384;    // one workgroup up to this many pairs
 constexpr int kSlice = 4096;               // pairs per slice in the multi-block path
 constexpr int kRoutePlanMaxPairs = 16384;  // fused top-k + plan: pairs kept in LDS
-constexpr int kRoutePlanMaxTokens = 64;    // ... and at most 4 tokens per wave
+// ... and at most 16 tokens (one per wave): with more, the one-workgroup plan is slower
+// than the top-k and permute launches it replaces (measured per layer at the decode
+// shape, k = 8: 6 us faster separate at 48 tokens, 9 us at 64, 11 us at the batched
+// T = 64 workload; the same at 16 tokens)
+constexpr int kRoutePlanMaxTokens = 16;
 
 // Exclusive scan of v (one value per thread for threads < 256) across the first four
 // waves; returns the exclusive prefix, and the total through *total. Must be called

@@ -1,24 +1,30 @@
 #!/usr/bin/env python3
 """Bench of the W4A16 MoE layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config decode_t8]
+    python bench.py [--steps K] [--warmup W] [--config long_prefill]
 
-A step is one MoE layer call (route -> permute -> expert up -> expert down ->
-combine+RMSNorm) over one batch of synthetic tokens, inputs resident in HBM. The
-default workload is decode with T=8 tokens (H=2048, E=128 experts, top-8, I=768,
-router logits computed from BF16 router weights). Weight copies are rotated so
-the working set is at least 1 GiB, which keeps the 256 MB Infinity Cache from
-serving the weights.
+A step is one pass of the whole MoE layer (route -> permute -> expert up -> expert
+down (+ the shared expert) -> combine+RMSNorm) over one batch of synthetic tokens,
+inputs resident in HBM. The default workload is long prefill: 32768 tokens as 4
+layer calls of 8192 (H=6144, 160 routed experts top-8 with Zipf(1.1) popularity,
+plus one shared expert, I=2048), the largest configuration that fits one GPU; a
+step is the 4 calls. ``--config`` selects another workload (tiny, decode_t1,
+decode_t8, batched_t64, batched_t256, prefill). Weight copies are rotated so the
+working set is at least 1 GiB, which keeps the 256 MB Infinity Cache from serving
+the weights.
 
-Two timed passes:
-  1. the headline: K fused ``moe4_layer`` calls between two events on the launch
-     stream (value = tokens / s, ms_per_step);
-  2. the roofline: the dominant kernel (the expert "up" pass, W13 + SwiGLU) launched
-     K times back to back on each chunk's plan, rotating weight copies, between two
+Timed passes:
+  1. the headline: K steps of fused ``moe4_layer`` calls between two events on the
+     launch stream (value = tokens / s, ms_per_step);
+  2. the roofline: the dominant kernel (the routed expert "up" pass, W13 + SwiGLU)
+     launched back to back on each chunk's plan, rotating weight copies, between two
      events on the launch stream; its algorithmic bytes (touched experts' packed
      weights + scales, activations in, h out) or flops divided by the mean launch
-     duration give ``roofline.achieved``.
-The fp64 oracle is timed on the host on a bounded sample (``cpu_baseline``).
+     duration give ``roofline.achieved``;
+  3. the other expert-FFN launches of a layer call (routed down; shared up and down),
+     timed the same way, reported under ``kernels``.
+The fp64 oracle is timed on the host (``cpu_baseline``) on a bounded sample of the
+same tokens, one worker process per host core, before the GPU is touched.
 Prints one JSON line.
 
 ``--op add_rmsnorm|group_rmsnorm`` times one of the neighbouring RMSNorm glue
@@ -46,11 +52,11 @@ MALL_DEFEAT_BYTES = 1 << 30
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--config", default="decode_t8")
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (0 = about 2 s of GPU work)")
+    ap.add_argument("--warmup", type=int, default=-1, help="untimed steps (-1 = steps / 10)")
+    ap.add_argument("--config", default="long_prefill")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample budget (per worker)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--side-stream", choices=["on", "off"], default="off",
                     help="routed chain on a side stream beside the shared expert (moe4_layer_side)")
@@ -64,7 +70,7 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ffn_up_decode_t8_traffic.md")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {"decode": os.path.join(ROOT, "bit_moe_expert_amd", "csrc", "ffn_decode.hip"),
                   "prefill": os.path.join(ROOT, "bit_moe_expert_amd", "csrc", "ffn_prefill.hip")}
 
@@ -76,67 +82,112 @@ def source_sha(path):
 
 
 def measured_traffic(config, kernel_source):
-    """HBM bytes per launch of the dominant kernel from the committed counter summary,
-    if it was taken on this workload with the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+    """HBM bytes per launch of the dominant kernel from a committed counter summary
+    (``profiles/*_traffic.md``, its ``machine:`` line), if one was taken on this
+    workload with the current kernel source; else None."""
+    if not os.path.isdir(PROFILES):
         return None
-    vals = {}
-    for line in open(TRAFFIC_SUMMARY):
-        if line.startswith("machine:"):
-            for kv in line[len("machine:"):].split():
-                k, _, v = kv.partition("=")
-                vals[k] = v
-    if vals.get("config") != config or vals.get("source_sha") != source_sha(kernel_source):
-        return None
-    return int(vals["traffic_bytes"])
+    want = source_sha(kernel_source)
+    for name in sorted(os.listdir(PROFILES)):
+        if not name.endswith("_traffic.md"):
+            continue
+        vals = {}
+        for line in open(os.path.join(PROFILES, name)):
+            if line.startswith("machine:"):
+                for kv in line[len("machine:"):].split():
+                    k, _, v = kv.partition("=")
+                    vals[k] = v
+        if vals.get("config") == config and vals.get("source_sha") == want:
+            return int(vals["traffic_bytes"])
+    return None
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def up_kernel_work(inp, idx):
-    """Algorithmic bytes and flops of one expert-up launch for this routing."""
-    w = inp.w
-    distinct = len(set(idx.reshape(-1).tolist()))
-    per_expert = 2 * w.I * w.H // 2 + 2 * w.I * w.H // 16 + 4   # nibbles + E4M3 scales + tscale
-    pairs = inp.T * w.k
-    act_in = inp.T * w.H * 2                                    # x, each token read once
-    h_out = pairs * w.I * 2
-    plan = (w.E + 1) * 4 + pairs * 4
-    nbytes = distinct * per_expert + act_in + h_out + plan
-    flops = 2 * pairs * w.H * (2 * w.I)
-    if w.n_shared:
-        nbytes += per_expert + inp.T * w.I * 2
-        flops += 2 * inp.T * w.H * 2 * w.I
-    return nbytes, flops, distinct
+def ffn_work(w, T, idx, up, dense):
+    """Algorithmic bytes and flops of one expert-FFN launch: the routed groups of the
+    plan (dense False; ``idx`` the routing) or the shared expert over all T tokens.
+    Bytes: the touched experts' packed codes + E4M3 scales + tensor scale, the
+    activations read (x once per token for up; h rows for down), the outputs written,
+    and the plan."""
+    N, K = (2 * w.I, w.H) if up else (w.H, w.I)
+    per_expert = N * K // 2 + N * K // 16 + 4
+    if dense:
+        rows, experts, plan = T, 1, 0
+    else:
+        rows = T * w.k
+        experts = len(set(idx.reshape(-1).tolist()))
+        plan = (w.E + 1) * 4 + (rows * 4 if up else 0)
+    act_in = T * w.H * 2 if up else rows * w.I * 2
+    out = rows * (w.I if up else w.H) * 2
+    nbytes = experts * per_expert + act_in + out + plan
+    flops = 2 * rows * N * K
+    return nbytes, flops, experts
 
 
-def cpu_baseline(inp, budget_s):
-    """Time the oracle as it stands on the host, one thread, on a bounded sample."""
-    import numpy as np
+_CPU = {}
+
+
+def _oracle_worker(wid, calls, budget_s):
+    """One host core's share of the oracle baseline: layer calls on its own token
+    subsets (tokens are independent) until the budget is spent."""
     from threadpoolctl import threadpool_limits
 
     import oracle
-    T = inp.T
-    per_call = T
-    sample_tokens = None
-    if inp.w.T > 64:  # prefill shapes: a seeded sample of tokens
-        sample_tokens = np.sort(np.random.default_rng(7).choice(inp.T, 16, replace=False))
-        per_call = len(sample_tokens)
-    reps, t_used = 0, 0.0
+    inputs = _CPU["inputs"]
+    done, t0 = 0, time.perf_counter()
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            oracle.layer(inp, tokens=sample_tokens)
-            reps += 1
-            t_used = time.perf_counter() - t0
-            if t_used >= budget_s or reps >= 1000:
+        for chunk, tokens in calls:
+            oracle.layer(inputs[chunk], tokens=tokens)
+            done += len(tokens)
+            if time.perf_counter() - t0 >= budget_s:
                 break
-    what = (f"{reps} oracle layer calls on the same {per_call}-token batch"
-            if sample_tokens is None else f"{reps} oracle calls on 16 sampled tokens of the {T}-token batch")
-    return {"value": reps * per_call / t_used, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what}; numpy fp64 with BLAS limited to 1 thread; {t_used:.1f} s"}
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(inputs, budget_s):
+    """Time the oracle as it stands on all host cores: one worker process per core
+    (forked before the GPU is initialised), each running oracle.layer on its own
+    seeded subsets of the workload's tokens, BLAS one thread per worker."""
+    import multiprocessing
+
+    import numpy as np
+    # the host cores this process may use: its affinity mask, capped by the thread
+    # budget the environment sets for the job (OMP_NUM_THREADS) where it sets one
+    cores = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    cores = min(cores, cap) if cap > 0 else cores
+    T, chunks = inputs[0].T, len(inputs)
+    # tokens per oracle call: the whole batch split over the cores for small batches,
+    # else two (a call dequantises every expert its tokens touch, seconds each)
+    per_call = max(1, min(2, T // cores)) if T >= 2 * cores else max(1, -(-T // cores))
+    rng = np.random.default_rng(7)
+    perms = [rng.permutation(T) for _ in range(chunks)]
+    cursor = [0] * chunks
+    calls_per_worker = 64
+    plans = []
+    for w in range(cores):
+        calls = []
+        for i in range(calls_per_worker):
+            c = (w + i) % chunks
+            p = cursor[c]
+            cursor[c] += per_call
+            calls.append((c, np.unique(perms[c][np.arange(p, p + per_call) % T])))
+        plans.append(calls)
+    _CPU["inputs"] = inputs
+    ctx = multiprocessing.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        res = pool.starmap(_oracle_worker, [(w, plans[w], budget_s) for w in range(cores)])
+    wall = time.perf_counter() - t0
+    _CPU.clear()
+    tokens = sum(r[0] for r in res)
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{tokens} token evaluations: seeded subsets of the {T * chunks}-token workload "
+                      f"(all chunks, cycling), oracle layer calls of up to {per_call} tokens on {cores} "
+                      f"worker processes (one per host core, BLAS 1 thread each), {wall:.1f} s wall"}
 
 
 def glue_main(args):
@@ -255,33 +306,38 @@ def main():
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (got --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    import torch
+    # counting devices does not initialise the GPU runtime (the oracle's worker
+    # processes are forked before anything does)
+    if torch.cuda.device_count() < 1:
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
     if args.op != "layer":
-        import torch
-        if not torch.cuda.is_available():
-            print("bench.py needs a GPU", file=sys.stderr)
-            sys.exit(1)
         torch.cuda.set_device(0)
         glue_main(args)
         return
 
     import numpy as np
-    import torch
 
     from bit_moe_expert_amd import binding as B
     from bit_moe_expert_amd import workloads as wl
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    torch.cuda.set_device(0)
     w = wl.workload(args.config)
     chunks = w.chunks
     log(f"generating inputs: {w}")
     t_gen = time.perf_counter()
-    inputs = [wl.make_inputs(w, seed=0, chunk=c) for c in range(chunks)] if chunks > 1 else [wl.make_inputs(w, seed=0)]
+    inputs = [wl.make_inputs(w, seed=0, chunk=0)]
+    for c in range(1, chunks):
+        inputs.append(wl.make_inputs(w, seed=0, chunk=c, weights_from=inputs[0]))
     inp = inputs[0]
     log(f"inputs ready in {time.perf_counter() - t_gen:.1f} s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on every host core for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(inputs, args.cpu_seconds)
+        log(f"cpu baseline: {cpu['value']:.2f} tokens/s on {cpu['cores']} cores")
 
+    torch.cuda.set_device(0)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
     w13 = B.DeviceW4.from_host(inp.w13)
     w2 = B.DeviceW4.from_host(inp.w2)
@@ -327,77 +383,120 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     calls_per_step = chunks
-    log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup * calls_per_step):
+    # steps: given, or about 2 s of GPU work from one timed probe step
+    for i in range(calls_per_step):
+        layer_step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(calls_per_step):
+        layer_step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    probe_s = max(ev0.elapsed_time(ev1) / 1e3, 1e-6)
+    steps = args.steps or int(min(2000, max(20, 2.0 / probe_s)))
+    warmup = args.warmup if args.warmup >= 0 else max(2, steps // 10)
+    log(f"warmup {warmup} steps, then {steps} timed")
+    for i in range(warmup * calls_per_step):
         layer_step(i)
     torch.cuda.synchronize()
 
     # ---- pass 1: headline ----
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps * calls_per_step):
+    for i in range(steps * calls_per_step):
         layer_step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = ev0.elapsed_time(ev1)
-    ms_per_step = ms_total / args.steps
+    ms_per_step = ms_total / steps
     tokens_per_step = T * chunks
-    value = tokens_per_step * args.steps / (ms_total / 1e3)
+    value = tokens_per_step * steps / (ms_total / 1e3)
     log(f"pass 1: {ms_per_step * 1e3:.2f} us/step, {value:.1f} tokens/s (wall {wall:.3f} s)")
 
-    # ---- pass 2: dominant kernel (expert up) timed with events ----
-    # The plan of every chunk is built first; then K2 up launches run back to back
+    # ---- passes 2 and 3: the expert-FFN launches, each timed with events ----
+    # The plan of every chunk is built first; then each launch kind runs back to back
     # (rotating weight copies as in pass 1) between two events on the launch stream,
     # so the mean is the kernel's own duration plus the gap between launches, not the
-    # events' overhead.
+    # events' overhead. The routed up launch (pass 2) is the dominant kernel.
     pairs = T * w.k
     pws_n = B.moe4_permute_workspace_bytes(shape)
     pws = torch.empty(pws_n, dtype=torch.uint8, device="cuda") if pws_n else None
-    h = torch.empty((pairs, w.I), dtype=torch.int16, device="cuda")
-    plans, routing = [], []
+    plans, routing, hs, hds = [], [], [], []
     for c in per_chunk:
         offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
         perm_src = torch.empty(pairs, dtype=torch.int32, device="cuda")
         inv = torch.empty(pairs, dtype=torch.int32, device="cuda")
         B.moe4_route(shape, c["x"] if wr is not None else None, wr, c["logits"], topk_idx, topk_w)
         B.moe4_permute(shape, topk_idx, offsets, perm_src, inv, pws)
+        h = torch.empty((pairs, w.I), dtype=torch.int16, device="cuda")
+        B.moe4_expert_up(shape, c["x"], offsets, perm_src, w13, h)
+        hs.append(h)
+        if s13 is not None:
+            hd = torch.empty((T, w.I), dtype=torch.int16, device="cuda")
+            B.moe4_expert_up(shape, c["x"], None, None, s13, hd)
+            hds.append(hd)
         torch.cuda.synchronize()
         routing.append(topk_idx.cpu().numpy())
         plans.append((offsets, perm_src))
-    k2 = min(args.steps, 400)
+    y = torch.empty((pairs, w.H), dtype=torch.int16, device="cuda")
+    yd = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
+    h_tmp = torch.empty((pairs, w.I), dtype=torch.int16, device="cuda")
+    hd_tmp = torch.empty((T, w.I), dtype=torch.int16, device="cuda")
 
-    def up_launch(i):
+    def up_routed(i):
         c = per_chunk[i % chunks]
         offsets, perm_src = plans[i % chunks]
-        a13, _ = weights[(i // chunks) % copies]
-        B.moe4_expert_up(shape, c["x"], offsets, perm_src, a13, h)
+        B.moe4_expert_up(shape, c["x"], offsets, perm_src, weights[(i // chunks) % copies][0], h_tmp)
 
-    for i in range(min(k2, 20) * chunks):
-        up_launch(i)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(k2 * chunks):
-        up_launch(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    up_mean_s = ev0.elapsed_time(ev1) / (k2 * chunks) / 1e3
-    n_up = k2 * chunks
-    nbytes, flops, distinct = 0, 0, []
-    for ci, idx in zip(inputs, routing):
-        b, f, d = up_kernel_work(ci, idx)
-        nbytes += b
-        flops += f
-        distinct.append(d)
-    nbytes /= chunks
-    flops /= chunks
-    log(f"pass 2: expert-up mean {up_mean_s * 1e6:.2f} us over {n_up} back-to-back launches; "
-        f"{nbytes / 1e6:.1f} MB, {flops / 1e9:.2f} GFLOP per launch; distinct experts {distinct}")
+    def down_routed(i):
+        offsets, _ = plans[i % chunks]
+        B.moe4_expert_down(shape, hs[i % chunks], offsets, weights[(i // chunks) % copies][1], y)
 
-    hbm_bound = flops / nbytes < 300.0
-    if hbm_bound:
+    def up_shared(i):
+        B.moe4_expert_up(shape, per_chunk[i % chunks]["x"], None, None, s13, hd_tmp)
+
+    def down_shared(i):
+        B.moe4_expert_down(shape, hds[i % chunks], None, s2, yd)
+
+    prefill_kind = T * w.k >= 40 * w.E
+    kind_name = "ffn_prefill_kernel" if prefill_kind else "ffn_decode_kernel"
+    launches = [("up_routed", up_routed, True, False), ("down_routed", down_routed, False, False)]
+    if s13 is not None:
+        launches += [("up_shared", up_shared, True, True), ("down_shared", down_shared, False, True)]
+    k2 = min(steps, 400)
+    kernels = {}
+    for name, fn, up, dense in launches:
+        for i in range(min(k2, 10) * chunks):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(k2 * chunks):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        mean_s = ev0.elapsed_time(ev1) / (k2 * chunks) / 1e3
+        nb = fl = 0
+        for idx in routing:
+            b, f, _ = ffn_work(w, T, idx, up, dense)
+            nb += b
+            fl += f
+        nb /= chunks
+        fl /= chunks
+        kernels[name] = {"kernel": f"{kind_name}<{str(up).lower()}, {str(dense).lower()}>"
+                                   if prefill_kind else f"{kind_name}<{str(up).lower()}, ...>",
+                         "mean_us": round(mean_s * 1e6, 3), "launches": k2 * chunks,
+                         "algorithmic_bytes": int(nb), "algorithmic_flops": int(fl),
+                         "GB_s": round(nb / mean_s / 1e9, 1), "TFLOP_s": round(fl / mean_s / 1e12, 1)}
+        log(f"pass {2 if name == 'up_routed' else 3}: {name} mean {mean_s * 1e6:.2f} us over {k2 * chunks} "
+            f"launches; {nb / 1e6:.1f} MB, {fl / 1e9:.2f} GFLOP per launch -> {nb / mean_s / 1e9:.0f} GB/s, "
+            f"{fl / mean_s / 1e12:.1f} TFLOP/s")
+
+    dom = kernels["up_routed"]
+    up_mean_s = dom["mean_us"] / 1e6
+    nbytes, flops = dom["algorithmic_bytes"], dom["algorithmic_flops"]
+    if not prefill_kind:
         achieved = nbytes / up_mean_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
@@ -405,12 +504,13 @@ def main():
         achieved = flops / up_mean_s / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
-    kind = "decode" if inp.T * w.k < 64 * w.E else "prefill"
-    roofline["traffic"] = measured_traffic(args.config, KERNEL_SOURCES[kind])
-    roofline.update({"kernel": ("ffn_decode_kernel<true>" if kind == "decode" else "ffn_prefill_kernel<true>")
-                               + " (expert up: W13 dequant-MFMA + SwiGLU)",
-                     "mean_us": round(up_mean_s * 1e6, 3), "algorithmic_bytes": int(nbytes),
+    roofline["traffic"] = measured_traffic(args.config, KERNEL_SOURCES["prefill" if prefill_kind else "decode"])
+    roofline.update({"kernel": dom["kernel"] + " (routed expert up: W13 dequant-MFMA + SwiGLU)",
+                     "mean_us": dom["mean_us"], "algorithmic_bytes": int(nbytes),
                      "algorithmic_flops": int(flops)})
+    for v in kernels.values():
+        v["frac_of_peak"] = round(v["TFLOP_s"] / BF16_PEAK_TFLOPS if prefill_kind else
+                                  v["GB_s"] / HBM_PEAK_GBS, 4)
 
     cfg = {"workload": f"{args.config}: T={T}{'x%d chunks' % chunks if chunks > 1 else ''} H={w.H} "
                        f"E={w.E}{'+%d shared' % w.n_shared if w.n_shared else ''} top-{w.k} I={w.I}, "
@@ -418,12 +518,11 @@ def main():
            "T": T * chunks, "H": w.H, "E": w.E, "k": w.k, "I": w.I, "n_shared": w.n_shared,
            "weight_copies_rotated": copies, "routing": w.routing, "side_stream": use_side}
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+           "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-           "data": "synthetic", "config": cfg, "roofline": roofline}
-    if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+           "data": "synthetic", "config": cfg, "roofline": roofline, "kernels": kernels}
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

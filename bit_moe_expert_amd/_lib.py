@@ -25,8 +25,12 @@ class Shape(Structure):
                 ("I", c_int32), ("n_shared", c_int32), ("eps", c_float)]
 
 
+MOE4_W4_CANONICAL = 1
+MOE4_W4_TILED = 2
+
+
 class W4(Structure):
-    _fields_ = [("packed", c_void_p), ("scales", c_void_p), ("tscale", c_void_p)]
+    _fields_ = [("packed", c_void_p), ("scales", c_void_p), ("tscale", c_void_p), ("layout", c_int32)]
 
 
 _SHAPE = POINTER(Shape)
@@ -61,7 +65,7 @@ SIGNATURES = {
                                    c_void_p]),
 }
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 _lib = None
 
 

@@ -52,32 +52,40 @@ def moe4_prepack_w4(G: int, N: int, K: int, codes, scales, tcodes, tscales, stre
 
 @dataclass
 class DeviceW4:
-    """A grouped 4-bit weight tensor resident on the GPU, in the tiled layout the
-    expert FFN reads (same bytes as the canonical layout, re-laid out once)."""
-    packed: torch.Tensor   # uint8 [G, N, K/2] bytes, tiled
-    scales: torch.Tensor   # uint8 [G, N, K/16] bytes, tiled
+    """A grouped 4-bit weight tensor resident on the GPU, in the tiled layout (the
+    canonical bytes re-laid out once by moe4_prepack_w4, faster to stream) or in the
+    canonical (checkpoint) layout as uploaded."""
+    packed: torch.Tensor   # uint8 [G, N, K/2] bytes
+    scales: torch.Tensor   # uint8 [G, N, K/16] bytes
     tscale: torch.Tensor   # float32 [G]
+    layout: int = _lib.MOE4_W4_TILED
 
     @classmethod
-    def from_host(cls, w, device="cuda") -> "DeviceW4":
-        """Upload canonical host weights (packed [G,N,K/2], scales [G,N,K/16]) and tile them."""
+    def from_host(cls, w, device="cuda", layout: str = "tiled") -> "DeviceW4":
+        """Upload canonical host weights (packed [G,N,K/2], scales [G,N,K/16]); with
+        layout="tiled" re-lay them out on the GPU, with "canonical" keep them as they are."""
         G, N, K2 = w.packed.shape
         codes = torch.from_numpy(w.packed).to(device)
         scales = torch.from_numpy(w.scales).to(device)
+        tscale = torch.from_numpy(w.tscale).to(device)
+        if layout == "canonical":
+            return cls(codes, scales, tscale, _lib.MOE4_W4_CANONICAL)
+        if layout != "tiled":
+            raise ValueError(f"layout must be 'tiled' or 'canonical', not {layout!r}")
         tcodes = torch.empty_like(codes)
         tscales = torch.empty_like(scales)
         moe4_prepack_w4(G, N, 2 * K2, codes, scales, tcodes, tscales)
         torch.cuda.current_stream().synchronize()
         del codes, scales
-        return cls(tcodes, tscales, torch.from_numpy(w.tscale).to(device))
+        return cls(tcodes, tscales, tscale, _lib.MOE4_W4_TILED)
 
     def clone(self) -> "DeviceW4":
-        return DeviceW4(self.packed.clone(), self.scales.clone(), self.tscale.clone())
+        return DeviceW4(self.packed.clone(), self.scales.clone(), self.tscale.clone(), self.layout)
 
     def desc(self) -> W4:
         return W4(_ptr(self.packed, "packed", (torch.uint8,)),
                   _ptr(self.scales, "scales", (torch.uint8,)),
-                  _ptr(self.tscale, "tscale", (torch.float32,)))
+                  _ptr(self.tscale, "tscale", (torch.float32,)), self.layout)
 
     @property
     def nbytes(self) -> int:

@@ -64,10 +64,16 @@ moe4_status check_w4(const moe4_w4* w, const char* name) {
   if (w->tscale == nullptr) return fail(MOE4_ERR_INVALID_ARG, "%s is NULL", buf);
   if (reinterpret_cast<uintptr_t>(w->tscale) & 3u)
     return fail(MOE4_ERR_INVALID_ARG, "%s is not 4-byte aligned", buf);
+  if (w->layout != MOE4_W4_CANONICAL && w->layout != MOE4_W4_TILED)
+    return fail(MOE4_ERR_INVALID_ARG,
+                "%s.layout is %d: must be MOE4_W4_CANONICAL (%d) or MOE4_W4_TILED (%d)", name, w->layout,
+                (int)MOE4_W4_CANONICAL, (int)MOE4_W4_TILED);
   return MOE4_OK;
 }
 
-moe4::W4View view(const moe4_w4* w) { return moe4::W4View{w->packed, w->scales, w->tscale}; }
+moe4::W4View view(const moe4_w4* w) {
+  return moe4::W4View{w->packed, w->scales, w->tscale, w->layout == MOE4_W4_TILED};
+}
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 

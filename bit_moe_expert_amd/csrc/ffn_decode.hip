@@ -7,9 +7,11 @@
 // kernel streams every touched tile once per 16 rows of its expert and nothing else
 // from HBM.
 //
-// Weights are in the tiled layout (prepack.hip): a 16-row x 128-column tile is 1 KB
+// Weights come in the tiled layout (prepack.hip): a 16-row x 128-column tile is 1 KB
 // of codes + 128 B of scales, stored in the lane order of the 16x16x32 BF16 MFMA
-// operand, so each wave reads a tile with one contiguous 1 KB load and one 128 B load.
+// operand, so each wave reads a tile with one contiguous 1 KB load and one 128 B load;
+// or in the canonical (checkpoint) layout, where the same loads gather 16 rows of 64
+// code bytes and 8 scale bytes.
 //
 // Work split. A wave owns a pair of 16-row blocks (up: a gate block and the matching
 // up block, so SwiGLU is applied in registers; down: two consecutive W2 blocks) and
@@ -52,6 +54,7 @@ struct DecodeArgs {
   int compact;              // units index the non-empty experts (T*k < G)
   int slots;                // C: workgroups per round of the placement
   int stage_rows;           // LDS form: activation rows staged (all of act)
+  int tiled;                // weights in the tiled layout, else canonical
 };
 
 constexpr int kSlices = 4;  // fixed K slices (see the accumulation order below)
@@ -245,6 +248,14 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   const BufRes rc1 = make_res(a.tcodes + tile1 * 1024, NS * 1024);
   const BufRes rs0 = make_res(a.tscales + tile0 * 128, NS * 128);
   const BufRes rs1 = make_res(a.tscales + tile1 * 128, NS * 128);
+  // Both layouts keep a 16-row block's codes (16 * K/2 bytes) and scales (16 * K/16)
+  // in one contiguous range at the same place; within it, this lane's 16 code bytes
+  // and 2 scale bytes of K step s sit at s * step + lane offset: tiled, one 1 KB +
+  // 128 B tile per step in lane order; canonical, row rn's 64 code bytes and 8 scale
+  // bytes of the step, columns 32kq..32kq+31 of them.
+  const int c_lane = a.tiled ? lane * 16 : rn * (K / 2) + kq * 16;
+  const int s_lane = a.tiled ? lane * 2 : rn * (K / 16) + kq * 2;
+  const int c_step = a.tiled ? 1024 : 64, s_step = a.tiled ? 128 : 8;
   // K is cut into kSlices fixed slices whose partial sums are always added as
   // ((s0 + s1) + s2) + s3, whichever waves computed them: the bits of a row do not
   // depend on ksplit, i.e. on how many tokens share the call.
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   auto issue = [&](Stage<kX>& t, int s) {
     s = s < s_end ? s : s_end - 1;
     s = s > 0 ? s : 0;
-    const int co = s * 1024 + lane * 16, so = s * 128 + lane * 2;
+    const int co = s * c_step + c_lane, so = s * s_step + s_lane;
     t.c0 = load_b128_nt(rc0, co);
     t.c1 = load_b128_nt(rc1, co);
     t.s0 = load_b16(rs0, so);
@@ -654,7 +665,8 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
 hipError_t launch_ffn_up_decode(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
                          int T, int G, int H, int I, W4View w13, uint16_t* h, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  DecodeArgs a{x, offsets, perm_src, k, T, w13.packed, w13.scales, w13.tscale, 2 * I, H, I, 1, h, G, 0, 1, 0};
+  DecodeArgs a{x, offsets, perm_src, k, T, w13.packed, w13.scales, w13.tscale, 2 * I, H, I, 1, h, G, 0, 1, 0,
+               w13.tiled ? 1 : 0};
   const long long active = offsets ? std::min<long long>((long long)T * k, G) : 1;
   return launch(true, a, active, offsets ? G : 1, T, T, s);
 }
@@ -662,7 +674,8 @@ hipError_t launch_ffn_up_decode(const uint16_t* x, const int32_t* offsets, const
 hipError_t launch_ffn_down_decode(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H, int I,
                            W4View w2, uint16_t* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  DecodeArgs a{h, offsets, nullptr, 1, T, w2.packed, w2.scales, w2.tscale, H, I, I, 1, y, G, 0, 1, 0};
+  DecodeArgs a{h, offsets, nullptr, 1, T, w2.packed, w2.scales, w2.tscale, H, I, I, 1, y, G, 0, 1, 0,
+               w2.tiled ? 1 : 0};
   const long long rows = offsets ? (long long)T * k : T;
   const long long active = offsets ? std::min<long long>((long long)T * k, G) : 1;
   return launch(false, a, active, offsets ? G : 1, rows, T, s);

@@ -21,7 +21,8 @@
 // per SIMD, and the activation rows past 192 (or 128) are neither loaded nor stored.
 //
 // Pipeline. Activation rows (gathered through perm_src for the up projection) and
-// weight half-tiles (tiled layout, 512 contiguous bytes per 16-row block) are loaded
+// weight half-tiles (tiled layout: 512 contiguous bytes per 16-row block; canonical:
+// 16 rows of 32 bytes) are loaded
 // into one of two register sets two steps ahead of use; during step i's MFMAs, step
 // i+1's set is dequantised (code * E4M3 scale is exact in BF16) and written to the
 // other LDS buffer part by part, each part's registers then refilled with step i+3.
@@ -67,6 +68,7 @@ struct GemmArgs {
   uint16_t* out;            // up: h [R][I]; down: y [R][N]
   int n_tiles;              // output column tiles per expert
   int total;                // grid size (multiple of kXcds)
+  int tiled;                // weights in the tiled layout, else canonical
 };
 
 // LDS tiles are [rows][64] BF16, 128 bytes a row; the 16-byte chunk c of row r is stored
@@ -78,7 +80,11 @@ struct GemmArgs {
 // groups of 8 rows. The key depends only on r % 16.
 __device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <bool kUp>
+// kDense: one group of T rows, row r = token r (the shared expert); else the routed
+// groups of the plan. (Separate instantiations, so that a kernel trace lists the
+// routed and the shared launches apart.) kTiled: the weights' layout (tiled, else
+// canonical); a compile-time choice, so the tiled form's addressing stays shifts.
+template <bool kUp, bool kDense, bool kTiled>
 __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BN * BK];
@@ -129,7 +135,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
         if (q >= n_h) q = -1;
       }
     };
-    if (a.offsets) {
+    if constexpr (!kDense) {
       int incl_f[kMaxExperts / 64], incl_t[kMaxExperts / 64], incl_h[kMaxExperts / 64];
       int first[kMaxExperts / 64], count[kMaxExperts / 64];  // expert 64c + lane's rows
       int carry_f = 0, carry_t = 0, carry_h = 0;
@@ -224,13 +230,19 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int rr = (tid >> 3) + 64 * i;
     int src = row0 + (rr < rows ? rr : 0);
-    if (kUp && a.perm_src) src = a.perm_src[src] / a.k;
+    if (kUp && !kDense) src = a.perm_src[src] / a.k;
     a_src[i] = a.act + (size_t)src * K + a_chunk * 8;
   }
-  // B: unit u = tid: 16-row block u/32, lane-in-half-tile u%32
+  // B: unit u = tid: 16-row block u/32, lane-in-half-tile u%32 (row rn = u%16 of the
+  // block, columns 32kq'..32kq'+31 of each 64-column step, kq' = (u%32)/16). Both
+  // layouts keep a block's codes (16 * K/2 bytes) and scales (16 * K/16) in one range
+  // at the same place; step st's 16 code bytes and 2 scale bytes of the unit sit at
+  // st * step + unit offset: tiled, 512 + 64 bytes a step (half a 16 x 128 tile) in
+  // lane order; canonical, 32 code bytes and 4 scale bytes a step along row rn.
   const uint8_t* b_code[1];
   const uint8_t* b_scale[1];
   int b_st[1];  // LDS element offset of the unit's row (its 4 chunks are 4*kq' + j)
+  constexpr int bc_step = kTiled ? 512 : 32, bs_step = kTiled ? 64 : 4;
 #pragma unroll
   for (int h = 0; h < 1; ++h) {
     const int u = tid;
@@ -239,8 +251,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
     if (kUp) wblk = blk < 8 ? (nt * 128) / 16 + blk : (a.I + nt * 128) / 16 + (blk - 8);
     else wblk = (nt * BN) / 16 + blk;
     const size_t tile = ((size_t)g * NB + wblk) * NS;
-    b_code[h] = a.tcodes + tile * 1024 + l * 16;
-    b_scale[h] = a.tscales + tile * 128 + l * 2;
+    const int rn = l & 15, kq = l >> 4;
+    b_code[h] = a.tcodes + tile * 1024 + (kTiled ? l * 16 : rn * (K / 2) + kq * 16);
+    b_scale[h] = a.tscales + tile * 128 + (kTiled ? l * 2 : rn * (K / 16) + kq * 2);
     b_st[h] = blk * 16 + (l & 15);
   }
   const int b_kq = (tid & 31) >> 4;  // same for both units
@@ -264,8 +277,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
     const int k0 = st * BK;
     if (q < groups) ra[S][q] = *reinterpret_cast<const u32x4*>(a_src[q] + k0);
     if (q == 3) {
-      const size_t toff = (size_t)(st >> 1) * 1024 + (st & 1) * 512;
-      const size_t soff = (size_t)(st >> 1) * 128 + (st & 1) * 64;
+      // (tiled: st * 512 and st * 64, written per 1 KB tile and half, which the
+      // compiler turns into fewer live registers than the product)
+      const size_t toff = kTiled ? (size_t)(st >> 1) * 1024 + (st & 1) * 512 : (size_t)st * bc_step;
+      const size_t soff = kTiled ? (size_t)(st >> 1) * 128 + (st & 1) * 64 : (size_t)st * bs_step;
       rb[S] = *reinterpret_cast<const u32x4*>(b_code[0] + toff);
       rs[S] = *reinterpret_cast<const uint16_t*>(b_scale[0] + soff);
     }
@@ -406,8 +421,19 @@ hipError_t launch(bool up, GemmArgs a, long long m_tiles, hipStream_t s) {
   const long long tiles = m_tiles * a.n_tiles;
   // each of the three runs of an XCD (full, three-quarter, half tiles) may round up by one
   a.total = (int)((tiles + kXcds - 1) / kXcds * kXcds) + 3 * kXcds;
-  if (up) hipLaunchKernelGGL(ffn_prefill_kernel<true>, dim3(a.total), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(ffn_prefill_kernel<false>, dim3(a.total), dim3(kThreads), 0, s, a);
+  const dim3 g(a.total), b(kThreads);
+  const bool dense = a.offsets == nullptr;
+  if (a.tiled) {
+    if (!dense && up) hipLaunchKernelGGL((ffn_prefill_kernel<true, false, true>), g, b, 0, s, a);
+    if (!dense && !up) hipLaunchKernelGGL((ffn_prefill_kernel<false, false, true>), g, b, 0, s, a);
+    if (dense && up) hipLaunchKernelGGL((ffn_prefill_kernel<true, true, true>), g, b, 0, s, a);
+    if (dense && !up) hipLaunchKernelGGL((ffn_prefill_kernel<false, true, true>), g, b, 0, s, a);
+  } else {
+    if (!dense && up) hipLaunchKernelGGL((ffn_prefill_kernel<true, false, false>), g, b, 0, s, a);
+    if (!dense && !up) hipLaunchKernelGGL((ffn_prefill_kernel<false, false, false>), g, b, 0, s, a);
+    if (dense && up) hipLaunchKernelGGL((ffn_prefill_kernel<true, true, false>), g, b, 0, s, a);
+    if (dense && !up) hipLaunchKernelGGL((ffn_prefill_kernel<false, true, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -423,14 +449,16 @@ bool prefill_shape_ok(int H, int I) { return H % BN == 0 && I % 128 == 0; }
 hipError_t launch_ffn_up_prefill(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
                                  int T, int G, int H, int I, W4View w13, uint16_t* h, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  GemmArgs a{x, offsets, perm_src, k, T, w13.packed, w13.scales, w13.tscale, 2 * I, H, I, G, h, 0, 0};
+  GemmArgs a{x, offsets, perm_src, k, T, w13.packed, w13.scales, w13.tscale, 2 * I, H, I, G, h, 0, 0,
+             w13.tiled ? 1 : 0};
   return launch(true, a, m_tile_bound(offsets, T, k, G), s);
 }
 
 hipError_t launch_ffn_down_prefill(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H,
                                    int I, W4View w2, uint16_t* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  GemmArgs a{h, offsets, nullptr, 1, T, w2.packed, w2.scales, w2.tscale, H, I, I, G, y, 0, 0};
+  GemmArgs a{h, offsets, nullptr, 1, T, w2.packed, w2.scales, w2.tscale, H, I, I, G, y, 0, 0,
+             w2.tiled ? 1 : 0};
   return launch(false, a, m_tile_bound(offsets, T, k, G), s);
 }
 

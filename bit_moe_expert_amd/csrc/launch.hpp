@@ -30,11 +30,12 @@ hipError_t launch_route_plan(const float* logits, int T, int E, int k, int32_t* 
 hipError_t launch_prepack(const uint8_t* codes, const uint8_t* scales, int G, int N, int K,
                           uint8_t* tcodes, uint8_t* tscales, hipStream_t s);
 
-// Grouped W4A16 FFN halves; weights in the tiled layout.
+// Grouped W4A16 FFN halves; weights in the tiled or the canonical layout.
 struct W4View {
   const uint8_t* packed;
   const uint8_t* scales;
   const float* tscale;
+  bool tiled;  // tiled (moe4_prepack_w4) layout, else canonical [G][N][K/2] / [G][N][K/16]
 };
 // h[r] = silu(gate . x[tok(r)]) * (up . x[tok(r)]); offsets/perm_src NULL = dense (G=1, R=T).
 // y[r] = W2 . h[r]. The dispatchers pick the decode (streaming) or the prefill (GEMM)

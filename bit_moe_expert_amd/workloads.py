@@ -212,12 +212,15 @@ class LayerInputs:
         return self.x.shape[0]
 
 
-def make_inputs(w: Workload, seed: int = 0, chunk: int = 0, T: Optional[int] = None) -> LayerInputs:
+def make_inputs(w: Workload, seed: int = 0, chunk: int = 0, T: Optional[int] = None,
+                weights_from: Optional["LayerInputs"] = None) -> LayerInputs:
     """Inputs of one layer call of workload ``w``.
 
     ``chunk`` selects the token chunk of a chunked workload: weights, router and
     gamma are the same for every chunk; activations, residual and logits differ.
-    ``T`` overrides the token count (for reduced-size tests).
+    ``T`` overrides the token count (for reduced-size tests). ``weights_from`` (the
+    inputs of another chunk of the same workload and seed) reuses its weights, router
+    and gamma instead of drawing them again: the draws would be the same.
     """
     T = w.T if T is None else T
     root = np.random.SeedSequence(seed)
@@ -226,18 +229,25 @@ def make_inputs(w: Workload, seed: int = 0, chunk: int = 0, T: Optional[int] = N
     s_tok = np.random.SeedSequence([seed, 7919, chunk])
     s_x, s_res, s_logits = s_tok.spawn(3)
 
-    gamma_rng = np.random.default_rng(s_gamma)
-    gamma = to_bf16_bits(gamma_rng.uniform(0.5, 1.5, w.H))
     x = _bf16_normal(np.random.default_rng(s_x), (T, w.H))
     residual = _bf16_normal(np.random.default_rng(s_res), (T, w.H))
+    logits = None
+    if w.routing != "router":
+        logits = _draw_logits(s_logits, w, T)
+    if weights_from is not None:
+        if weights_from.w != w or weights_from.seed != seed:
+            raise ValueError("weights_from must be inputs of the same workload and seed")
+        b = weights_from
+        return LayerInputs(w=w, x=x, residual=residual, gamma=b.gamma, w13=b.w13, w2=b.w2,
+                           logits=logits, w_router=b.w_router, shared13=b.shared13,
+                           shared2=b.shared2, seed=seed)
+    gamma_rng = np.random.default_rng(s_gamma)
+    gamma = to_bf16_bits(gamma_rng.uniform(0.5, 1.5, w.H))
     w13 = draw_w4(s_w13, w.E, 2 * w.I, w.H)
     w2 = draw_w4(s_w2, w.E, w.H, w.I)
-    logits = None
     w_router = None
     if w.routing == "router":
         w_router = _bf16_normal(np.random.default_rng(s_router), (w.E, w.H), std=w.router_std)
-    else:
-        logits = _draw_logits(s_logits, w, T)
     shared13 = shared2 = None
     if w.n_shared:
         shared13 = draw_w4(s_sh13, w.n_shared, 2 * w.I, w.H)

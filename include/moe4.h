@@ -21,15 +21,19 @@
  *   projection.  W2 (per expert): N = H rows, K = I.  The shared expert uses the same
  *   layouts with one expert.
  *
- * Weight layouts. The layout above is the canonical (checkpoint) layout. The expert
- * FFN entry points read the TILED layout that moe4_prepack_w4 produces from it once,
- * at weight-load time: the same bytes, moved so that every 16-row x 128-column tile
- * is 1 KB of codes plus 128 B of scales in the order the MFMA operands consume them.
- * Tile (g, b, s) (expert g, rows 16b..16b+15, columns 128s..128s+127) sits at tile
- * index (g * N/16 + b) * K/128 + s; within it, lane l = rn + 16*kq (rn = l % 16,
- * kq = l / 16) owns code bytes 16l..16l+15 = canonical row 16b+rn, columns
- * 128s+32kq..+31, and scale bytes 2l, 2l+1 = that row's scales for column groups
- * 8s+2kq and 8s+2kq+1. The tensor scales are not moved.
+ * Weight layouts. The layout above is the CANONICAL (checkpoint) layout: NVFP4 as a
+ * checkpoint stores it, read as is without re-quantisation (bear-blog article on
+ * TensorFold 1.0.12 / PR804, section "What PR804 does and does not do"). The expert
+ * FFN entry points accept it, and also the TILED layout that moe4_prepack_w4
+ * produces from it once, at weight-load time: the same bytes, moved so that every
+ * 16-row x 128-column tile is 1 KB of codes plus 128 B of scales in the order the
+ * MFMA operands consume them, which streams faster (one contiguous 1 KB read per
+ * wave instead of 16 rows of 64 bytes). Tile (g, b, s) (expert g, rows 16b..16b+15,
+ * columns 128s..128s+127) sits at tile index (g * N/16 + b) * K/128 + s; within it,
+ * lane l = rn + 16*kq (rn = l % 16, kq = l / 16) owns code bytes 16l..16l+15 =
+ * canonical row 16b+rn, columns 128s+32kq..+31, and scale bytes 2l, 2l+1 = that row's
+ * scales for column groups 8s+2kq and 8s+2kq+1. The tensor scales are not moved.
+ * Each weight descriptor names its layout (moe4_w4.layout); both give the same bits.
  *
  * The expert FFN is SwiGLU: h = silu(gate . x) * (up . x), y = W2 . h.
  * Routing: softmax over the E logits, the k largest selected (ties -> lower expert
@@ -69,7 +73,7 @@
 extern "C" {
 #endif
 
-#define MOE4_ABI_VERSION 1
+#define MOE4_ABI_VERSION 2
 
 typedef enum {
   MOE4_OK = 0,
@@ -90,13 +94,24 @@ typedef struct {
   float eps;        /* RMSNorm epsilon (> 0) */
 } moe4_shape;
 
+/* Layout of a weight descriptor's codes and scales. There is no default: a
+ * descriptor whose layout is neither value (e.g. a zero-initialised one) is rejected
+ * with MOE4_ERR_INVALID_ARG, so bytes of one layout cannot be read as the other
+ * without the caller having said so. */
+typedef enum {
+  MOE4_W4_CANONICAL = 1, /* [G][N][K/2] codes, [G][N][K/16] scales, row-major (checkpoint) */
+  MOE4_W4_TILED = 2      /* the same bytes re-laid out by moe4_prepack_w4 (faster to stream) */
+} moe4_w4_layout;
+
 /* One grouped 4-bit weight tensor over G experts (host struct of device pointers).
- * packed: G*N*K/2 code bytes and scales: G*N*K/16 E4M3 bytes, both in the TILED layout
- * (see moe4_prepack_w4); tscale [G] FP32. */
+ * packed: G*N*K/2 code bytes and scales: G*N*K/16 E4M3 bytes, both in `layout`;
+ * tscale [G] FP32. packed is 16-byte aligned, scales 2-byte aligned, tscale 4-byte
+ * aligned. */
 typedef struct {
   const uint8_t* packed;
   const uint8_t* scales;
   const float* tscale;
+  int32_t layout; /* a moe4_w4_layout value */
 } moe4_w4;
 
 /* Version of this header the library was built from (MOE4_ABI_VERSION). */

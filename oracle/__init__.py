@@ -44,7 +44,9 @@ Readings where the pages are silent (each is stated again where it is used):
       over the whole row; there is no gate (the pages name none). G = H is R10.
 
 Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
-(closed forms, library routines, brute force on tiny inputs, invariants).
+(closed forms, library routines, brute force on tiny inputs, invariants); ``layer``
+with a shared expert is pinned against an independent torch composition, and
+``tests/test_oracle_mutations.py`` checks that planted mistakes fail a pin.
 """
 from __future__ import annotations
 
@@ -192,7 +194,9 @@ def swiglu_hidden(x: np.ndarray, w13: np.ndarray) -> np.ndarray:
     I = w13.shape[0] // 2
     g = x @ w13[:I].T
     u = x @ w13[I:].T
-    return g / (1.0 + np.exp(-g)) * u
+    # e^-g overflows to inf for g < -709; g / inf is then the correct (signed) zero
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
 
 
 def swiglu_ffn(x: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:

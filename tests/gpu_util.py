@@ -95,11 +95,11 @@ class GpuLayer:
         }
 
 
-def upload_weights(inp: wl.LayerInputs):
-    w13 = B.DeviceW4.from_host(inp.w13)
-    w2 = B.DeviceW4.from_host(inp.w2)
-    s13 = B.DeviceW4.from_host(inp.shared13) if inp.shared13 is not None else None
-    s2 = B.DeviceW4.from_host(inp.shared2) if inp.shared2 is not None else None
+def upload_weights(inp: wl.LayerInputs, layout: str = "tiled"):
+    w13 = B.DeviceW4.from_host(inp.w13, layout=layout)
+    w2 = B.DeviceW4.from_host(inp.w2, layout=layout)
+    s13 = B.DeviceW4.from_host(inp.shared13, layout=layout) if inp.shared13 is not None else None
+    s2 = B.DeviceW4.from_host(inp.shared2, layout=layout) if inp.shared2 is not None else None
     wr = to_dev(inp.w_router) if inp.w_router is not None else None
     return w13, w2, s13, s2, wr
 

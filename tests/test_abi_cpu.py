@@ -36,9 +36,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert _lib.load().moe4_abi_version() == 1
+    assert _lib.load().moe4_abi_version() == 2
     m = re.search(r"#define MOE4_ABI_VERSION (\d+)", open(HEADER).read())
-    assert int(m.group(1)) == 1
+    assert int(m.group(1)) == 2
 
 
 def shape(**kw):
@@ -93,8 +93,8 @@ def test_null_and_misaligned_pointers():
     assert lib.moe4_route(s, FAKE + 2, FAKE, FAKE, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
     assert b"aligned" in lib.moe4_last_error()
     assert lib.moe4_permute(s, FAKE, None, FAKE, FAKE, None, 0, None) == _lib.MOE4_ERR_INVALID_ARG
-    w = W4(FAKE, FAKE, FAKE)
-    nul = W4(FAKE, None, FAKE)
+    w = W4(FAKE, FAKE, FAKE, _lib.MOE4_W4_TILED)
+    nul = W4(FAKE, None, FAKE, _lib.MOE4_W4_TILED)
     assert lib.moe4_expert_ffn(s, FAKE, FAKE, None, w, w, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
     assert lib.moe4_expert_ffn(s, FAKE, FAKE, FAKE, w, nul, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
     assert b"w2.scales" in lib.moe4_last_error()
@@ -112,7 +112,7 @@ def test_permute_workspace_too_small():
 def test_layer_workspace_and_shared_checks():
     lib = _lib.load()
     s = shape()
-    w = W4(FAKE, FAKE, FAKE)
+    w = W4(FAKE, FAKE, FAKE, _lib.MOE4_W4_TILED)
     need = lib.moe4_layer_workspace_bytes(s)
     st = lib.moe4_layer(s, FAKE, None, FAKE, w, w, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                         FAKE, need - 1, None)
@@ -128,7 +128,7 @@ def test_layer_side_needs_events():
     before anything is enqueued (the stream handles are never used)."""
     lib = _lib.load()
     sh = shape(n_shared=1)
-    w = W4(FAKE, FAKE, FAKE)
+    w = W4(FAKE, FAKE, FAKE, _lib.MOE4_W4_TILED)
     side = ctypes.c_void_p(0x2000)
     st = lib.moe4_layer_side(sh, FAKE, None, FAKE, w, w, w, w, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                              FAKE, 1 << 40, None, side, None, FAKE)
@@ -175,3 +175,34 @@ def test_rmsnorm_glue_checks():
     # T == 0 does nothing, NULL buffers included
     assert lib.moe4_add_rmsnorm(0, 64, None, None, None, 1e-6, None, None, None) == OK
     assert lib.moe4_group_rmsnorm(0, 64, 16, None, None, 1e-6, None, None) == OK
+
+
+@pytest.mark.parametrize("layout", [0, 3, -1, 0x7FFFFFFF])
+def test_weight_layout_tag_is_required(layout):
+    """A weight descriptor must name its layout (canonical or tiled): an untagged
+    (zero-initialised) or unknown tag is rejected before anything is enqueued, in
+    every entry point that reads weights."""
+    lib = _lib.load()
+    s = shape()
+    good = W4(FAKE, FAKE, FAKE, _lib.MOE4_W4_TILED)
+    bad = W4(FAKE, FAKE, FAKE, layout)
+    E_ARG = _lib.MOE4_ERR_INVALID_ARG
+    assert lib.moe4_expert_ffn(s, FAKE, FAKE, FAKE, bad, good, FAKE, FAKE, None) == E_ARG
+    assert b"w13.layout" in lib.moe4_last_error()
+    assert lib.moe4_expert_ffn(s, FAKE, FAKE, FAKE, good, bad, FAKE, FAKE, None) == E_ARG
+    assert b"w2.layout" in lib.moe4_last_error()
+    assert lib.moe4_expert_up(s, FAKE, FAKE, FAKE, bad, FAKE, None) == E_ARG
+    assert lib.moe4_expert_down(s, FAKE, FAKE, bad, FAKE, None) == E_ARG
+    st = lib.moe4_layer(s, FAKE, None, FAKE, good, bad, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, 1 << 40, None)
+    assert st == E_ARG and b"w2.layout" in lib.moe4_last_error()
+    sh = shape(n_shared=1)
+    st = lib.moe4_layer(sh, FAKE, None, FAKE, good, good, bad, good, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, 1 << 40, None)
+    assert st == E_ARG and b"shared13.layout" in lib.moe4_last_error()
+    # both named layouts pass the descriptor check (the call then fails on the workspace)
+    for lay in (_lib.MOE4_W4_CANONICAL, _lib.MOE4_W4_TILED):
+        w = W4(FAKE, FAKE, FAKE, lay)
+        st = lib.moe4_layer(s, FAKE, None, FAKE, w, w, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, 16, None)
+        assert st == _lib.MOE4_ERR_WORKSPACE

@@ -245,17 +245,28 @@ def _plan_on_host(inp):
     return idx, w, off, perm, inv
 
 
-def _check_routed_ffn(inp, w, off, perm):
-    """Runs moe4_expert_ffn on the plan (off, perm) and checks h against the oracle's
-    SwiGLU and y against the oracle's down projection of the GPU's own h."""
+def _run_routed_ffn(inp, w, off, perm, layout="tiled"):
+    """moe4_expert_ffn on the plan (off, perm) with the weights in `layout`; h, y bits."""
     shape = B.make_shape(inp.T, w.H, w.E, w.k, w.I)
-    w13, w2, *_ = upload_weights(inp)
+    w13, w2, *_ = upload_weights(inp, layout)
     R = inp.T * w.k
     h = torch.zeros((R, w.I), dtype=torch.int16, device="cuda")
     y = torch.zeros((R, w.H), dtype=torch.int16, device="cuda")
     B.moe4_expert_ffn(shape, to_dev(inp.x), to_dev(off), to_dev(perm), w13, w2, h, y)
     torch.cuda.synchronize()
-    got_h, got_y = bf16_f64(h), bf16_f64(y)
+    return to_host_bits(h), to_host_bits(y)
+
+
+def _check_routed_ffn(inp, w, off, perm, canonical_too=True):
+    """Runs moe4_expert_ffn on the plan (off, perm) and checks h against the oracle's
+    SwiGLU and y against the oracle's down projection of the GPU's own h. With the
+    weights in the canonical layout the same kernels must give the same bits."""
+    h_bits, y_bits = _run_routed_ffn(inp, w, off, perm)
+    if canonical_too:
+        ch, cy = _run_routed_ffn(inp, w, off, perm, "canonical")
+        assert np.array_equal(ch, h_bits), "h differs between the canonical and the tiled layout"
+        assert np.array_equal(cy, y_bits), "y differs between the canonical and the tiled layout"
+    got_h, got_y = oracle.bf16_value(h_bits), oracle.bf16_value(y_bits)
     x = oracle.bf16_value(inp.x)
     tok = perm // w.k
     exp_of_row = np.repeat(np.arange(w.E), np.diff(off))
@@ -316,10 +327,48 @@ def test_expert_ffn_prefill_schedule_edges():
     _check_routed_ffn(inp, w, off, perm)
 
 
-@pytest.mark.parametrize("T", [77, 200, 300])
+WIDE_CASES = ["decode_t8", "expert_staged", "expert8_passes", "batched_t64"]
+
+
+@pytest.mark.parametrize("name", WIDE_CASES)
+def test_expert_ffn_wide_range_rows(name):
+    """Activation rows of very different magnitudes (row scales 2^-50 .. 2^26) whose
+    values each span 2^31 below the row's largest: the staged forms of the streaming
+    kernel scale each row (or row slice) by its own power of two into FP16, which keeps
+    the BF16 result's bits while a row's values lie within 2^32 of its maximum. Each
+    row of h is checked against the oracle on its own scale (1 BF16 ulp plus 2^-12 of
+    the row's rms), and each row of y against fp64 sums over the GPU's own h."""
+    w = dict((c[0], c[1]) for c in FFN_CASES)[name] or wl.workload(name)
+    note(f"expert ffn wide-range rows: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
+    inp = wl.make_inputs(w, seed=8)
+    rng = np.random.default_rng(81)
+    row_scale = np.exp2(rng.uniform(-50, 26, (inp.T, 1)))
+    within = np.exp2(rng.uniform(-31, 0, (inp.T, w.H)))
+    inp.x[:] = wl.to_bf16_bits(rng.standard_normal((inp.T, w.H)) * within * row_scale)
+    idx, _, off, perm, inv = _plan_on_host(inp)
+    h_bits, y_bits = _run_routed_ffn(inp, w, off, perm)
+    got_h, got_y = oracle.bf16_value(h_bits), oracle.bf16_value(y_bits)
+    x = oracle.bf16_value(inp.x)
+    tok = perm // w.k
+    exp_of_row = np.repeat(np.arange(w.E), np.diff(off))
+    for e in np.unique(exp_of_row):
+        rows = np.flatnonzero(exp_of_row == e)
+        W13 = oracle.dequant(inp.w13.packed[e], inp.w13.scales[e], inp.w13.tscale[e])
+        W2 = oracle.dequant(inp.w2.packed[e], inp.w2.scales[e], inp.w2.tscale[e])
+        ref_h = oracle.bf16_round(oracle.swiglu_hidden(x[tok[rows]], W13))
+        ref_y = oracle.bf16_round(got_h[rows] @ W2.T)
+        for i, r in enumerate(rows):
+            assert_bf16_close(got_h[r], ref_h[i], f"h row {r} (expert {e})", min_equal=0.8)
+            assert_bf16_close(got_y[r], ref_y[i], f"y row {r} (expert {e})", slack_rms=2.0 ** -16,
+                              min_equal=0.8)
+
+
+@pytest.mark.parametrize("T", [1, 8, 17, 39, 77, 200, 300])
 def test_expert_ffn_dense_shared(T):
-    """Dense (shared expert) mode on the prefill GEMM: one half tile (77 rows), one
-    padded full tile (200) and a full tile plus a half one (300)."""
+    """Dense (shared expert) mode: on the streaming kernel below 40 rows (1, 8, 17 and
+    39 rows: one or several 16-row passes, a ragged last one), and on the prefill GEMM
+    from 40: one half tile (77 rows), one padded full tile (200) and a full tile plus a
+    half one (300)."""
     w = wl.Workload("shared_small", T=T, H=1024, E=1, k=1, I=512, routing="normal")
     note(f"expert ffn dense (shared expert mode) T={T}")
     inp = wl.make_inputs(w, seed=2)
@@ -440,7 +489,7 @@ def test_combine_norm_closed_form_zero_experts():
 # Whole layer
 # ----------------------------------------------------------------------------
 LAYER_CASES = [("tiny", None), ("decode_t1", None), ("decode_t8", None), ("batched_t64", None),
-               ("batched_t256", None), ("prefill", 96), ("long_prefill", 24)]
+               ("batched_t256", None), ("prefill", 1024)]
 
 
 @pytest.mark.parametrize("name,sample", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
@@ -469,6 +518,121 @@ def test_layer_parity(name, sample):
     e_n = rel_rms_err(got["n"][sel], ref["n"])
     note(f"  rel-rms err o={e_o:.2e} n={e_n:.2e}")
     assert e_o <= LAYER_TOL and e_n <= LAYER_TOL
+
+
+def test_long_prefill_layer_parity_all_chunks():
+    """Long prefill, all four chunks of 8192 tokens (one shared set of weights): routing
+    of every token bit-exact; o and n of a seeded sample of 1024 tokens per chunk
+    within the bar of one oracle pass over the 4096 sampled tokens (tokens are
+    independent, so the oracle can take them together)."""
+    w = wl.workload("long_prefill")
+    note("layer parity: long prefill, 4 chunks x 8192 tokens, 1024 sampled per chunk")
+    base = wl.make_inputs(w, seed=0, chunk=0)
+    weights = upload_weights(base)
+    rng = np.random.default_rng(321)
+    parts, got_o, got_n, sizes = [], [], [], []
+    for c in range(w.chunks):
+        inp = base if c == 0 else wl.make_inputs(w, seed=0, chunk=c, weights_from=base)
+        g = GpuLayer(inp, weights=weights)
+        g.run()
+        got = g.host()
+        del g
+        L = inp.logits.astype(np.float64)
+        ref_idx, ref_w = oracle.route(L, w.k)
+        assert np.array_equal(got["idx"], ref_idx), f"chunk {c}: routing"
+        assert np.max(np.abs(got["w"] - ref_w)) <= 1e-5, f"chunk {c}: routing weights"
+        tok = np.sort(rng.choice(w.T, 1024, replace=False))
+        parts.append((inp.x[tok], inp.residual[tok], inp.logits[tok]))
+        got_o.append(got["o"][tok])
+        got_n.append(got["n"][tok])
+        note(f"  chunk {c}: GPU done, routing exact")
+    combined = dataclasses.replace(base, x=np.concatenate([p[0] for p in parts]),
+                                   residual=np.concatenate([p[1] for p in parts]),
+                                   logits=np.concatenate([p[2] for p in parts]))
+    ref = oracle.layer(combined)
+    for c in range(w.chunks):
+        sl = slice(1024 * c, 1024 * (c + 1))
+        e_o = rel_rms_err(got_o[c], ref["o"][sl])
+        e_n = rel_rms_err(got_n[c], ref["n"][sl])
+        note(f"  chunk {c}: rel-rms err o={e_o:.2e} n={e_n:.2e}")
+        assert e_o <= LAYER_TOL and e_n <= LAYER_TOL, f"chunk {c}"
+
+
+def _deq_pair(m13, m2, e):
+    return (oracle.dequant(m13.packed[e], m13.scales[e], m13.tscale[e]),
+            oracle.dequant(m2.packed[e], m2.scales[e], m2.tscale[e]))
+
+
+def _sample_plan_rows(off, rng):
+    """Rows of the plan to check, per expert: the first and last row, the first row and
+    a middle row of the last M tile (a half or three-quarter tile when the expert's
+    count is not a multiple of 256), and two random rows; plus every row of the
+    hottest expert and of one expert whose last tile is three-quarter (129-192 rows)
+    and one whose last tile is half (1-128 rows)."""
+    cnt = np.diff(off)
+    rows = []
+    for e in np.flatnonzero(cnt):
+        a, b = int(off[e]), int(off[e + 1])
+        lt = a + (cnt[e] - 1) // 256 * 256
+        rows += [a, b - 1, lt, (lt + b - 1) // 2, *rng.integers(a, b, 2)]
+    full = [int(np.argmax(cnt))]
+    rem = cnt % 256
+    for lo, hi in ((129, 192), (1, 128)):
+        cand = np.flatnonzero((rem >= lo) & (rem <= hi) & (cnt > 256))
+        cand = cand if cand.size else np.flatnonzero((rem >= lo) & (rem <= hi))
+        if cand.size:
+            full.append(int(cand[0]))
+    for e in full:
+        rows += list(range(int(off[e]), int(off[e + 1])))
+    return np.unique(np.array(rows, dtype=np.int64)), full
+
+
+@pytest.mark.parametrize("name", ["prefill", "long_prefill"])
+def test_expert_ffn_full_size_sampled_rows(name):
+    """The expert FFN at the full prefill and long-prefill shapes (8192 tokens, Zipf
+    routing, the real tile schedule with its three-quarter and half last tiles and its
+    per-XCD runs): h of sampled plan rows (see _sample_plan_rows) against the oracle's
+    SwiGLU, and y of the same rows against fp64 sums over the GPU's own h, at the
+    step-level bars; for long prefill also the shared expert (dense, 8192 rows)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    w = wl.workload(name)
+    inp = wl.make_inputs(w, seed=0, chunk=0)
+    idx, _, off, perm, inv = _plan_on_host(inp)
+    rng = np.random.default_rng(55)
+    rows, full = _sample_plan_rows(off, rng)
+    note(f"expert ffn full size: {name}: {rows.size} plan rows checked, every row of experts {full} "
+         f"(counts {[int(off[e + 1] - off[e]) for e in full]})")
+    h_bits, y_bits = _run_routed_ffn(inp, w, off, perm)
+    got_h, got_y = oracle.bf16_value(h_bits), oracle.bf16_value(y_bits)
+    del h_bits, y_bits
+    x = oracle.bf16_value(inp.x)
+    tok = perm // w.k
+    exp_of_row = np.repeat(np.arange(w.E), np.diff(off))
+
+    def check_expert(e):
+        rr = rows[exp_of_row[rows] == e]
+        if rr.size == 0:
+            return
+        W13, W2 = _deq_pair(inp.w13, inp.w2, e)
+        assert_bf16_close(got_h[rr], oracle.bf16_round(oracle.swiglu_hidden(x[tok[rr]], W13)), f"h expert {e}")
+        assert_bf16_close(got_y[rr], oracle.bf16_round(got_h[rr] @ W2.T), f"y expert {e}", slack_rms=2.0 ** -16)
+
+    with ThreadPoolExecutor(8) as ex:
+        list(ex.map(check_expert, range(w.E)))
+    if w.n_shared:
+        shape = B.make_shape(inp.T, w.H, 1, 1, w.I)
+        s13 = B.DeviceW4.from_host(inp.shared13)
+        s2 = B.DeviceW4.from_host(inp.shared2)
+        h = torch.zeros((inp.T, w.I), dtype=torch.int16, device="cuda")
+        y = torch.zeros((inp.T, w.H), dtype=torch.int16, device="cuda")
+        B.moe4_expert_ffn(shape, to_dev(inp.x), None, None, s13, s2, h, y)
+        torch.cuda.synchronize()
+        sr = np.unique(np.concatenate([[0, 255, 256, inp.T - 1], rng.integers(0, inp.T, 500)]))
+        sh, sy = bf16_f64(h)[sr], bf16_f64(y)[sr]
+        W13, W2 = _deq_pair(inp.shared13, inp.shared2, 0)
+        assert_bf16_close(sh, oracle.bf16_round(oracle.swiglu_hidden(x[sr], W13)), "shared h")
+        assert_bf16_close(sy, oracle.bf16_round(sh @ W2.T), "shared y", slack_rms=2.0 ** -16)
 
 
 def test_layer_deterministic_and_batch_independent():
@@ -568,6 +732,16 @@ def test_layer_matches_entry_points(name, w):
     assert np.array_equal(off.cpu().numpy(), ref_off) and np.array_equal(perm.cpu().numpy(), ref_perm)
 
 
+def _check_against_oracle(inp, got):
+    """Routing bit-exact and outputs within the layer bar of the oracle (all tokens)."""
+    ref = oracle.layer(inp)
+    assert np.array_equal(got["idx"], ref["idx"])
+    assert np.max(np.abs(got["w"] - ref["w"])) <= 1e-5
+    e_o, e_n = rel_rms_err(got["o"], ref["o"]), rel_rms_err(got["n"], ref["n"])
+    note(f"  vs oracle: rel-rms err o={e_o:.2e} n={e_n:.2e}")
+    assert e_o <= LAYER_TOL and e_n <= LAYER_TOL
+
+
 GRAPH_CASES = [
     ("decode_t8", None),
     ("prefill_small", wl.Workload("prefill_small", T=1024, H=1024, E=16, k=4, I=384, routing="zipf")),
@@ -578,7 +752,7 @@ GRAPH_CASES = [
 def test_layer_graph_replay(name, w):
     """moe4_layer captured into a HIP graph (torch.cuda.CUDAGraph) and replayed several
     times, with eager calls and synchronisations in between: every replay must give
-    the eager call's bytes."""
+    the eager call's bytes, which match the oracle."""
     w = wl.workload(name) if w is None else w
     note(f"layer graph replay: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
     inp = wl.make_inputs(w, seed=4)
@@ -587,6 +761,7 @@ def test_layer_graph_replay(name, w):
     g = GpuLayer(inp)
     g.run()
     ref = g.host()
+    _check_against_oracle(inp, ref)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -623,12 +798,14 @@ SIDE_CASES = [
 @pytest.mark.parametrize("name,w", SIDE_CASES, ids=[c[0] for c in SIDE_CASES])
 def test_layer_side_stream(name, w):
     """moe4_layer_side (routed chain on a side stream, shared expert on the main stream)
-    gives moe4_layer's bytes, eagerly and captured into a HIP graph as a fork and join."""
+    gives moe4_layer's bytes, which match the oracle, eagerly and captured into a HIP
+    graph as a fork and join."""
     note(f"layer side stream: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} shared={w.n_shared}")
     inp = wl.make_inputs(w, seed=5)
     g = GpuLayer(inp)
     g.run()
     ref = g.host()
+    _check_against_oracle(inp, ref)
     side = torch.cuda.Stream()
     for _ in range(2):
         g.res_out.zero_()
@@ -649,6 +826,39 @@ def test_layer_side_stream(name, w):
         torch.cuda.synchronize()
         got = g.host()
         assert np.array_equal(got["o_bits"], ref["o_bits"]) and np.array_equal(got["n_bits"], ref["n_bits"])
+
+
+CANONICAL_CASES = [
+    ("tiny", None), ("decode_t8", None), ("batched_t64", None),
+    ("shared_prefill", wl.Workload("shared_prefill", T=1024, H=1024, E=8, k=2, I=256, routing="zipf",
+                                   n_shared=1)),
+    ("shared_decode", wl.Workload("shared_decode", T=8, H=1024, E=32, k=4, I=256, routing="normal",
+                                  n_shared=1)),
+]
+
+
+@pytest.mark.parametrize("name,w", CANONICAL_CASES, ids=[c[0] for c in CANONICAL_CASES])
+def test_layer_canonical_weights(name, w):
+    """moe4_layer on weights in the canonical (checkpoint) layout, read as they are:
+    the same bits as on the tiled layout, and within the bar of the oracle."""
+    w = wl.workload(name) if w is None else w
+    note(f"layer canonical weights: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} shared={w.n_shared}")
+    inp = wl.make_inputs(w, seed=6)
+    if w.routing == "router":
+        condition_router_margin(inp)
+    g = GpuLayer(inp, weights=upload_weights(inp, "canonical"))
+    g.run()
+    got = g.host()
+    gt = GpuLayer(inp)
+    gt.run()
+    ref_bits = gt.host()
+    assert np.array_equal(got["idx"], ref_bits["idx"])
+    assert np.array_equal(got["o_bits"], ref_bits["o_bits"]) and np.array_equal(got["n_bits"], ref_bits["n_bits"])
+    ref = oracle.layer(inp)
+    assert np.array_equal(got["idx"], ref["idx"])
+    e_o, e_n = rel_rms_err(got["o"], ref["o"]), rel_rms_err(got["n"], ref["n"])
+    note(f"  rel-rms err o={e_o:.2e} n={e_n:.2e}")
+    assert e_o <= LAYER_TOL and e_n <= LAYER_TOL
 
 
 def test_layer_t0_is_a_noop():

@@ -4,6 +4,8 @@ Each case plants one mistake in the oracle (monkeypatching a function of the
 ``oracle`` module, so the other oracle functions see it too) and checks that at
 least one of the pins in ``test_oracle_pins`` then fails.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -135,6 +137,46 @@ def _ffn_unrounded(x, w13, w2):
     return oracle.swiglu_hidden(x, w13) @ w2.T
 
 
+def _no_shared(inp):
+    return dataclasses.replace(inp, shared13=None, shared2=None)
+
+
+def _layer_with_shared(inp, tokens, cache, logits, shared_of):
+    """The original layer without its shared expert, then the combine redone with
+    shared_of(out, x) as the shared term."""
+    out = _orig["layer"](_no_shared(inp), tokens, cache, logits)
+    if inp.shared13 is None:
+        return out
+    tok = out["tokens"]
+    W13 = oracle.dequant(inp.shared13.packed[0], inp.shared13.scales[0], inp.shared13.tscale[0])
+    W2 = oracle.dequant(inp.shared2.packed[0], inp.shared2.scales[0], inp.shared2.tscale[0])
+    s = shared_of(out, oracle.bf16_value(np.asarray(inp.x)[tok]), W13, W2)
+    out["o"], out["n"] = oracle.combine_norm(out["y"], out["w"], np.asarray(inp.residual)[tok], inp.gamma,
+                                             inp.w.eps, s)
+    return out
+
+
+def _layer_shared_dropped(inp, tokens=None, cache=None, logits=None):
+    return _orig["layer"](_no_shared(inp), tokens, cache, logits)
+
+
+def _layer_shared_gated(inp, tokens=None, cache=None, logits=None):  # scaled by w_0
+    return _layer_with_shared(inp, tokens, cache, logits,
+                              lambda out, x, W13, W2: out["w"][:, :1] * oracle.swiglu_ffn(x, W13, W2))
+
+
+def _layer_shared_wrong_rows(inp, tokens=None, cache=None, logits=None):  # rows reversed
+    return _layer_with_shared(inp, tokens, cache, logits,
+                              lambda out, x, W13, W2: oracle.swiglu_ffn(x[::-1], W13, W2))
+
+
+def _layer_shared_up_as_gate(inp, tokens=None, cache=None, logits=None):  # halves swapped
+    def f(out, x, W13, W2):
+        I = W13.shape[0] // 2
+        return _orig["swiglu_ffn"](x, np.concatenate([W13[I:], W13[:I]]), W2)
+    return _layer_with_shared(inp, tokens, cache, logits, f)
+
+
 MUTANTS = {
     "bf16_round": [_bf16_truncate],
     "e2m1_value": [_e2m1_bias0],
@@ -149,6 +191,7 @@ MUTANTS = {
     "combine_norm": [_combine_no_residual, _combine_no_gamma, _combine_shared_dropped],
     "group_rmsnorm": [_group_norm_whole_row, _group_norm_no_eps, _group_norm_gamma_per_group],
     "add_rmsnorm": [_add_norm_of_x, _add_norm_no_residual],
+    "layer": [_layer_shared_dropped, _layer_shared_gated, _layer_shared_wrong_rows, _layer_shared_up_as_gate],
 }
 
 CASES = [(name, fn) for name, fns in MUTANTS.items() for fn in fns]

@@ -427,3 +427,59 @@ def test_layer_composition_matches_steps():
     assert np.array_equal(out["perm_src"], perm) and np.array_equal(out["inv"], inv)
     assert np.array_equal(out["offsets"], offsets)
     np.testing.assert_allclose(out["w"].sum(axis=1), 1.0, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# Whole layer with the shared expert (TensorFold issue #627, jschmied's Oct 14
+# comment: a shared expert runs beside the routed chain, ungated)
+# ----------------------------------------------------------------------------
+def _torch_dequant(m, e):
+    """One expert of a grouped 4-bit tensor, decoded with torch's float8 type for the
+    E4M3 scales and the OCP E2M1 table from the golden file (not the oracle's)."""
+    e2m1 = torch.tensor([v for _, v in read_golden("e2m1_values.txt")], dtype=torch.float64)
+    p = torch.from_numpy(m.packed[e].astype(np.int64))
+    codes = torch.stack([p & 15, p >> 4], dim=-1).reshape(p.shape[0], -1)
+    sc = torch.from_numpy(m.scales[e]).view(torch.float8_e4m3fn).to(torch.float64)
+    return e2m1[codes] * sc.repeat_interleave(16, dim=1) * float(m.tscale[e])
+
+
+def test_layer_with_shared_expert_matches_torch_composition():
+    """The layer with one shared expert, composed independently from torch library
+    ops: torch.topk + torch.softmax routing, a per-token loop over the selected
+    experts' SwiGLU FFNs (torch silu, BF16 activations), the shared expert's dense
+    SwiGLU FFN on every token with weight 1, the residual, then torch rms_norm."""
+    w = wl.Workload("shared_pin", T=7, H=128, E=6, k=2, I=128, routing="normal", n_shared=1)
+    inp = wl.make_inputs(w, seed=21)
+    out = oracle.layer(inp)
+    bf = lambda t: torch.from_numpy(oracle.bf16_round(t.numpy()))  # rounding pinned above
+    val = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double()
+    x, r, g = val(inp.x), val(inp.residual), val(inp.gamma)
+    L = torch.from_numpy(inp.logits.astype(np.float64))
+    sel = torch.topk(L, w.k, dim=1)  # margins >= 1e-3: no ties
+    p = torch.softmax(L, dim=1).gather(1, sel.indices)
+    p = p / p.sum(dim=1, keepdim=True)
+    I = w.I
+
+    def ffn(xr, W13, W2):
+        hmid = bf(torch.nn.functional.silu(xr @ W13[:I].T) * (xr @ W13[I:].T))
+        return bf(hmid @ W2.T)
+
+    experts = {e: (_torch_dequant(inp.w13, e), _torch_dequant(inp.w2, e)) for e in range(w.E)}
+    routed = torch.zeros((w.T, w.H), dtype=torch.float64)
+    for t in range(w.T):
+        for j in range(w.k):
+            e = int(sel.indices[t, j])
+            routed[t] += p[t, j] * ffn(x[t:t + 1], *experts[e])[0]
+    shared = ffn(x, _torch_dequant(inp.shared13, 0), _torch_dequant(inp.shared2, 0))
+    o = r + routed + shared
+    n = torch.nn.functional.rms_norm(o, (w.H,), weight=g, eps=w.eps)
+    assert np.array_equal(out["idx"], sel.indices.numpy())
+    np.testing.assert_allclose(out["w"], p.numpy(), rtol=1e-13)
+    np.testing.assert_allclose(out["o"], o.numpy(), rtol=1e-12, atol=1e-10)
+    np.testing.assert_allclose(out["n"], n.numpy(), rtol=1e-12, atol=1e-10)
+    # the shared term is not negligible here: leaving it out moves o by >> the bar
+    assert np.max(np.abs(shared.numpy())) > 100 * 1e-10
+    # a token subset gives the same rows (the shared expert sees the subset's own rows)
+    sub = oracle.layer(inp, tokens=np.array([5, 1]))
+    np.testing.assert_allclose(sub["o"], o.numpy()[[5, 1]], rtol=1e-12, atol=1e-10)
+    np.testing.assert_allclose(sub["n"], n.numpy()[[5, 1]], rtol=1e-12, atol=1e-10)

@@ -295,7 +295,8 @@ def layer(inp, tokens=None, cache=None, logits=None):
     With ``tokens`` only those rows are computed (routing, FFN, combine and norm are
     per token, so a subset is exact); the plan is then left out. ``logits``
     overrides the router (for reusing the fp64 logits of a previous call).
-    Returns a dict of fp64 / int32 arrays.
+    Returns a dict of fp64 / int32 arrays (``y`` the routed experts' outputs [T, k, H],
+    ``shared`` the shared expert's output [T, H] or None).
     """
     wl = inp.w
     T = inp.x.shape[0]
@@ -315,7 +316,8 @@ def layer(inp, tokens=None, cache=None, logits=None):
         W2 = dequant(inp.shared2.packed[0], inp.shared2.scales[0], inp.shared2.tscale[0])
         shared = swiglu_ffn(bf16_value(np.asarray(inp.x)[tok]), W13, W2)
     o, n = combine_norm(y, w, np.asarray(inp.residual)[tok], inp.gamma, wl.eps, shared)
-    out = {"logits": logits, "idx": idx, "w": w, "y": y, "o": o, "n": n, "tokens": tok}
+    out = {"logits": logits, "idx": idx, "w": w, "y": y, "o": o, "n": n, "tokens": tok,
+           "shared": shared}
     if tokens is None:
         out["offsets"], out["perm_src"], out["inv"] = permute(idx, wl.E)
     return out

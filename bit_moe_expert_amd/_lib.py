@@ -25,6 +25,7 @@ class Shape(Structure):
                 ("I", c_int32), ("n_shared", c_int32), ("eps", c_float)]
 
 
+MOE4_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE4_W4_CANONICAL = 1
 MOE4_W4_TILED = 2
 
@@ -56,6 +57,8 @@ SIGNATURES = {
     "moe4_layer": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, _W4, _W4, _W4, _W4, c_void_p,
                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                            c_void_p]),
+    "moe4_layer_noalloc": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, _W4, _W4, _W4, _W4, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe4_layer_side": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, _W4, _W4, _W4, _W4, c_void_p,
                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                 c_void_p, c_void_p, c_void_p, c_void_p]),

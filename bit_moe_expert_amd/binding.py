@@ -203,6 +203,25 @@ def moe4_layer(shape: Shape, x, w_router, logits, w13: DeviceW4, w2: DeviceW4,
     check(_lib.load().moe4_layer_side(*args, side_stream.cuda_stream, fork.cuda_event, join.cuda_event))
 
 
+def moe4_layer_noalloc(shape: Shape, x, w_router, logits, w13: DeviceW4, w2: DeviceW4,
+                       shared13: Optional[DeviceW4], shared2: Optional[DeviceW4], residual, gamma,
+                       topk_idx, topk_w, residual_out, normed_out, stream=None) -> None:
+    """The whole layer with the library's static per-GPU scratch instead of a workspace
+    (for callers that cannot allocate); shapes beyond its size are rejected."""
+    T, H, E, k = shape.T, shape.H, shape.E, shape.k
+    d13, d2 = w13.desc(), w2.desc()
+    s13 = shared13.desc() if shared13 is not None else None
+    s2 = shared2.desc() if shared2 is not None else None
+    check(_lib.load().moe4_layer_noalloc(
+        shape, _ptr(x, "x", _BF16_LIKE, T * H), _ptr(w_router, "w_router", _BF16_LIKE, E * H),
+        _ptr(logits, "logits", (torch.float32,), T * E), d13, d2, s13, s2,
+        _ptr(residual, "residual", _BF16_LIKE, T * H), _ptr(gamma, "gamma", _BF16_LIKE, H),
+        _ptr(topk_idx, "topk_idx", (torch.int32,), T * k),
+        _ptr(topk_w, "topk_w", (torch.float32,), T * k),
+        _ptr(residual_out, "residual_out", _BF16_LIKE, T * H),
+        _ptr(normed_out, "normed_out", _BF16_LIKE, T * H), _stream(stream)))
+
+
 _SIDE_EVENTS = {}
 
 

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe4.h"
 #include "launch.hpp"
 
@@ -94,6 +96,35 @@ LayerWs layer_ws_layout(const moe4_shape* s) {
   l.y = o;        o += align256(rows * s->H * 2);
   l.total = o;
   return l;
+}
+
+// Scratch of moe4_layer_noalloc: one file-scope device array, which every GPU the
+// library runs on holds until the process ends. Host code never passes `scratch`
+// itself to a kernel or a copy (on the host the name is a stand-in, not a device
+// address): the device address is looked up once per device with
+// hipGetSymbolAddress and kept in g_scratch_ptr.
+__device__ __align__(256) static uint8_t scratch[MOE4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch` (looked up on the first call on the device).
+moe4_status scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE4_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(MOE4_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE4_OK;
 }
 
 }  // namespace
@@ -342,12 +373,15 @@ moe4_status moe4_group_rmsnorm(int32_t T, int32_t H, int32_t group, const uint16
 }
 
 // The layer on `stream`, or with the routed chain on `side_stream` (see moe4_layer_side).
+// With use_scratch the workspace is the library's static scratch (moe4_layer_noalloc);
+// it is looked up only after every argument check has passed.
 static moe4_status layer_impl(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
                               float* logits, const moe4_w4* w13, const moe4_w4* w2,
                               const moe4_w4* shared13, const moe4_w4* shared2, const uint16_t* residual,
                               const uint16_t* gamma, int32_t* topk_idx, float* topk_w,
                               uint16_t* residual_out, uint16_t* normed_out, void* ws, size_t ws_bytes,
-                              void* stream, void* side_stream, void* fork_event, void* join_event) {
+                              void* stream, void* side_stream, void* fork_event, void* join_event,
+                              bool use_scratch = false) {
   g_err[0] = 0;
   moe4_status st = check_shape(shape);
   if (st) return st;
@@ -371,6 +405,15 @@ static moe4_status layer_impl(const moe4_shape* shape, const uint16_t* x, const 
   if (two_streams && (!fork_event || !join_event))
     return fail(MOE4_ERR_INVALID_ARG, "a side stream needs fork_event and join_event");
   const LayerWs L = layer_ws_layout(shape);
+  if (use_scratch) {
+    if (L.total > (size_t)MOE4_NOALLOC_SCRATCH_BYTES)
+      return fail(MOE4_ERR_UNSUPPORTED,
+                  "moe4_layer_noalloc: this shape needs %zu bytes of scratch, more than the %zu the "
+                  "library holds per GPU (use moe4_layer with a workspace)",
+                  L.total, (size_t)MOE4_NOALLOC_SCRATCH_BYTES);
+    if ((st = scratch_ptr(&ws))) return st;
+    ws_bytes = MOE4_NOALLOC_SCRATCH_BYTES;
+  }
   if (ws == nullptr || ws_bytes < L.total)
     return fail(MOE4_ERR_WORKSPACE, "layer needs %zu workspace bytes, got %zu%s", L.total, ws_bytes,
                 ws ? "" : " (NULL)");
@@ -444,6 +487,16 @@ moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_
                        size_t ws_bytes, void* stream) {
   return layer_impl(shape, x, w_router, logits, w13, w2, shared13, shared2, residual, gamma, topk_idx, topk_w,
                     residual_out, normed_out, ws, ws_bytes, stream, nullptr, nullptr, nullptr);
+}
+
+moe4_status moe4_layer_noalloc(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                               float* logits, const moe4_w4* w13, const moe4_w4* w2,
+                               const moe4_w4* shared13, const moe4_w4* shared2,
+                               const uint16_t* residual, const uint16_t* gamma, int32_t* topk_idx,
+                               float* topk_w, uint16_t* residual_out, uint16_t* normed_out,
+                               void* stream) {
+  return layer_impl(shape, x, w_router, logits, w13, w2, shared13, shared2, residual, gamma, topk_idx, topk_w,
+                    residual_out, normed_out, nullptr, 0, stream, nullptr, nullptr, nullptr, true);
 }
 
 moe4_status moe4_layer_side(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,

@@ -215,6 +215,28 @@ moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_
                        float* topk_w, uint16_t* residual_out, uint16_t* normed_out, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* moe4_layer for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same launches,
+ * with the plan, h and y in a scratch array of MOE4_NOALLOC_SCRATCH_BYTES that the
+ * library holds in each GPU's memory for the life of the process, instead of a
+ * caller workspace. Arguments as for moe4_layer, without ws and ws_bytes.
+ *   - Shapes whose layer workspace (moe4_layer_workspace_bytes) exceeds
+ *     MOE4_NOALLOC_SCRATCH_BYTES return MOE4_ERR_UNSUPPORTED (64 MiB holds decode and
+ *     batched decode up to a few thousand routed rows, e.g. 256 tokens x top-8 at
+ *     H = 4096, I = 2048; prefill shapes need moe4_layer).
+ *   - The call allocates and frees nothing. Its first call on a device looks the
+ *     array up (hipGetSymbolAddress); make that call outside graph capture.
+ *   - Every call on a GPU shares that GPU's array, and each call writes every byte of
+ *     it that it reads, so nothing has to be cleared between calls; but calls that
+ *     overlap on one GPU (other streams, other threads) race on it: order them. */
+#define MOE4_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe4_status moe4_layer_noalloc(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                               float* logits, const moe4_w4* w13, const moe4_w4* w2,
+                               const moe4_w4* shared13, const moe4_w4* shared2,
+                               const uint16_t* residual, const uint16_t* gamma, int32_t* topk_idx,
+                               float* topk_w, uint16_t* residual_out, uint16_t* normed_out,
+                               void* stream);
+
 /* The whole layer with the routed chain on a side stream (#627, jschmied's comment of
  * Oct 14 on where one step's time goes: the router, top-k, plan and routed experts run
  * on a side stream while the main stream runs the shared expert and then waits for

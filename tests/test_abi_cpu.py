@@ -206,3 +206,25 @@ def test_weight_layout_tag_is_required(layout):
         st = lib.moe4_layer(s, FAKE, None, FAKE, w, w, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                             FAKE, 16, None)
         assert st == _lib.MOE4_ERR_WORKSPACE
+
+
+def test_noalloc_layer_checks():
+    """moe4_layer_noalloc checks its arguments like moe4_layer, and rejects shapes whose
+    workspace exceeds its static scratch, all before any GPU call."""
+    lib = _lib.load()
+    w = W4(FAKE, FAKE, FAKE, _lib.MOE4_W4_TILED)
+    big = shape(T=8192, H=4096, E=128, I=1536)
+    assert lib.moe4_layer_workspace_bytes(big) > _lib.MOE4_NOALLOC_SCRATCH_BYTES
+    st = lib.moe4_layer_noalloc(big, FAKE, None, FAKE, w, w, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == _lib.MOE4_ERR_UNSUPPORTED and b"scratch" in lib.moe4_last_error()
+    s = shape()
+    st = lib.moe4_layer_noalloc(s, FAKE, None, None, w, w, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == _lib.MOE4_ERR_INVALID_ARG and b"logits" in lib.moe4_last_error()
+    bad = W4(FAKE, FAKE, FAKE, 0)
+    st = lib.moe4_layer_noalloc(s, FAKE, None, FAKE, w, bad, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == _lib.MOE4_ERR_INVALID_ARG and b"w2.layout" in lib.moe4_last_error()
+    assert lib.moe4_layer_noalloc(shape(T=0), None, None, None, None, None, None, None, None, None, None, None,
+                                  None, None, None) == _lib.MOE4_OK
+    # the header's scratch size is the one the binding knows
+    m = re.search(r"#define MOE4_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert int(m.group(1)) << int(m.group(2)) == _lib.MOE4_NOALLOC_SCRATCH_BYTES

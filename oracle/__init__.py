@@ -42,6 +42,17 @@ Readings where the pages are silent (each is stated again where it is used):
   R17 group_rmsnorm (named the same way) normalises each contiguous group of G
       columns of a row by that group's own mean square, then multiplies by one gamma
       over the whole row; there is no gate (the pages name none). G = H is R10.
+  R18 the FP8 prefill variant (W4A8; the Qiita TensorFold 1.1.x article, section
+      "Why it still does not reach 0.6.6", names an FP8 prompt-matmul option, and the
+      PR804 article's NVFP4 section tells W4A16 from lower-precision activations):
+      the FFN's matmul inputs are FP8 E4M3. Activations (x for the up projection, the
+      BF16 h for the down projection) are quantised in blocks of 32 consecutive
+      values along K, each block with its own power-of-two scale 2^e, e the smallest
+      integer for which the block's largest magnitude times 2^-e is at most 448 (no
+      saturation; e = 0 for an all-zero block; e clamped to [-127, 127]), the scaled
+      values rounded to E4M3 (nearest, ties to even). Weights: each code * block
+      scale (exact) rounded to E4M3 the same way, saturating at 448; the tensor scale
+      multiplies the sum. Sums are fp64; h and y are BF16 as in R11.
 
 Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
 (closed forms, library routines, brute force on tiny inputs, invariants); ``layer``
@@ -56,6 +67,8 @@ __all__ = [
     "bf16_value", "bf16_round", "e2m1_value", "e4m3_value", "unpack_codes", "dequant",
     "router_logits", "route", "permute", "swiglu_hidden", "swiglu_ffn", "expert_outputs",
     "combine_norm", "add_rmsnorm", "group_rmsnorm", "layer",
+    "e4m3_round", "mxfp8_quantize", "dequant_e4m3", "swiglu_hidden_w4a8", "swiglu_ffn_w4a8",
+    "layer_w4a8",
 ]
 
 
@@ -321,3 +334,102 @@ def layer(inp, tokens=None, cache=None, logits=None):
     if tokens is None:
         out["offsets"], out["perm_src"], out["inv"] = permute(idx, wl.E)
     return out
+
+
+# ----------------------------------------------------------------------------
+# FP8 (W4A8) prefill variant, reading R18
+# ----------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """fp64 -> the nearest OCP E4M3FN value (ties to even), saturating at +-448.
+
+    E4M3 keeps 4 significant bits for magnitudes from 2^-6 up and a fixed step of
+    2^-9 below (subnormals): with |v| = m * 2^e (1 <= m < 2, e >= -6 after
+    clamping), |v| * 2^(3-e) is rounded to an integer (np.rint: half to even).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(a)                 # a = f * 2^e with 0.5 <= f < 1
+    e = np.maximum(e - 1, -6)          # exponent of the leading bit, subnormals below 2^-6
+    r = np.ldexp(np.rint(np.ldexp(a, 3 - e)), e - 3)
+    return np.copysign(np.minimum(r, E4M3_MAX), v)
+
+
+def mxfp8_quantize(x: np.ndarray, block: int = 32):
+    """Block-scaled FP8 activations (reading R18): x [..., K] (K a multiple of block)
+    -> (q, e): q fp64 [..., K] E4M3 values and e int [..., K/block], x ~ q * 2^e.
+
+    Each block's scale exponent is the smallest e with max|x| * 2^-e <= 448: with
+    max|x| = m * 2^E (1 <= m < 2), e = E - 8 when m <= 1.75 (m * 2^8 <= 448) and
+    E - 7 otherwise; 0 for an all-zero block; clamped to [-127, 127].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    if K % block:
+        raise ValueError(f"K={K} is not a multiple of {block}")
+    xb = x.reshape(x.shape[:-1] + (K // block, block))
+    amax = np.max(np.abs(xb), axis=-1)
+    f, E = np.frexp(amax)              # amax = (2f) * 2^(E-1), 1 <= 2f < 2
+    e = np.where(2.0 * f <= 1.75, E - 1 - 8, E - 1 - 7)
+    e = np.where(amax == 0, 0, e)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    q = e4m3_round(np.ldexp(xb, -e[..., None]))
+    return q.reshape(x.shape), e
+
+
+def _mx_value(x: np.ndarray, block: int = 32) -> np.ndarray:
+    q, e = mxfp8_quantize(x, block)
+    return (q.reshape(e.shape + (block,)) * np.exp2(e)[..., None]).reshape(q.shape)
+
+
+def dequant_e4m3(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """One expert's 4-bit matrix with each weight (code * E4M3 block scale, exact)
+    rounded to E4M3 (reading R18) -> fp64 [N, K]; the tensor scale is left out (it
+    multiplies the sums)."""
+    return e4m3_round(dequant(packed, scales, 1.0))
+
+
+def swiglu_hidden_w4a8(x: np.ndarray, w13_8: np.ndarray, tscale: float) -> np.ndarray:
+    """a = silu(g) * u with g, u = tscale * (MXFP8(x) . W) over the E4M3 weights w13_8
+    [2I, H] (gate rows first); x [R, H] fp64 values."""
+    I = w13_8.shape[0] // 2
+    xq = _mx_value(x)
+    g = float(tscale) * (xq @ w13_8[:I].T)
+    u = float(tscale) * (xq @ w13_8[I:].T)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+def swiglu_ffn_w4a8(x, w13_8, ts13, w2_8, ts2) -> np.ndarray:
+    """y = ts2 * MXFP8(h) . W2_8 with h = BF16(swiglu_hidden_w4a8(x)); y rounded to BF16."""
+    h = bf16_round(swiglu_hidden_w4a8(x, w13_8, ts13))
+    return bf16_round(float(ts2) * (_mx_value(h) @ w2_8.T))
+
+
+def layer_w4a8(inp, tokens=None, logits=None):
+    """The whole layer with the W4A8 FFN (reading R18) for the routed experts and the
+    shared expert; routing, combine and norm as in ``layer``. Returns the same dict
+    (without the plan)."""
+    wl = inp.w
+    T = inp.x.shape[0]
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    if logits is None:
+        logits = (np.asarray(inp.logits, dtype=np.float64)[tok] if inp.logits is not None
+                  else router_logits(np.asarray(inp.x)[tok], inp.w_router))
+    idx, w = route(logits, wl.k)
+    x = bf16_value(np.asarray(inp.x)[tok])
+    y = np.zeros((len(tok), wl.k, x.shape[1]), dtype=np.float64)
+    for e in np.unique(idx):
+        rr, jj = np.nonzero(idx == e)
+        W13 = dequant_e4m3(inp.w13.packed[e], inp.w13.scales[e])
+        W2 = dequant_e4m3(inp.w2.packed[e], inp.w2.scales[e])
+        y[rr, jj] = swiglu_ffn_w4a8(x[rr], W13, inp.w13.tscale[e], W2, inp.w2.tscale[e])
+    shared = None
+    if getattr(inp, "shared13", None) is not None:
+        S13 = dequant_e4m3(inp.shared13.packed[0], inp.shared13.scales[0])
+        S2 = dequant_e4m3(inp.shared2.packed[0], inp.shared2.scales[0])
+        shared = swiglu_ffn_w4a8(x, S13, inp.shared13.tscale[0], S2, inp.shared2.tscale[0])
+    o, n = combine_norm(y, w, np.asarray(inp.residual)[tok], inp.gamma, wl.eps, shared)
+    return {"logits": logits, "idx": idx, "w": w, "y": y, "o": o, "n": n, "tokens": tok, "shared": shared}

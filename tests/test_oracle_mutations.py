@@ -177,6 +177,76 @@ def _layer_shared_up_as_gate(inp, tokens=None, cache=None, logits=None):  # halv
     return _layer_with_shared(inp, tokens, cache, logits, f)
 
 
+def _e4m3_truncate(v):  # rounds toward zero
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(a)
+    e = np.maximum(e - 1, -6)
+    return np.copysign(np.minimum(np.ldexp(np.trunc(np.ldexp(a, 3 - e)), e - 3), 448.0), v)
+
+
+def _e4m3_no_saturation(v):  # overflow rounds on past 448
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(a)
+    e = np.maximum(e - 1, -6)
+    return np.copysign(np.ldexp(np.rint(np.ldexp(a, 3 - e)), e - 3), v)
+
+
+def _e4m3_fnuz_subnormals(v):  # subnormal range starting one binade lower
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(a)
+    e = np.maximum(e - 1, -7)
+    return np.copysign(np.minimum(np.ldexp(np.rint(np.ldexp(a, 3 - e)), e - 3), 448.0), v)
+
+
+def _mx_scale_saturating(x, block=32):  # e = E - 8 always: large blocks saturate
+    x = np.asarray(x, dtype=np.float64)
+    xb = x.reshape(x.shape[:-1] + (x.shape[-1] // block, block))
+    amax = np.max(np.abs(xb), axis=-1)
+    _, E = np.frexp(amax)
+    e = np.where(amax == 0, 0, E - 1 - 8).astype(np.int64)
+    return oracle.e4m3_round(np.ldexp(xb, -e[..., None])).reshape(x.shape), e
+
+
+def _mx_block16(x, block=32):
+    q, e = _orig["mxfp8_quantize"](x, 16)
+    return q, e[..., ::2]
+
+
+def _dequant_e4m3_unrounded(packed, scales):
+    return oracle.dequant(packed, scales, 1.0)
+
+
+def _hidden_w4a8_unquantized(x, w13_8, tscale):
+    I = w13_8.shape[0] // 2
+    g = float(tscale) * (np.asarray(x) @ w13_8[:I].T)
+    u = float(tscale) * (np.asarray(x) @ w13_8[I:].T)
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def _hidden_w4a8_no_tscale(x, w13_8, tscale):
+    return _orig["swiglu_hidden_w4a8"](x, w13_8, 1.0)
+
+
+def _ffn_w4a8_h_unquantized(x, w13_8, ts13, w2_8, ts2):
+    h = oracle.bf16_round(oracle.swiglu_hidden_w4a8(x, w13_8, ts13))
+    return oracle.bf16_round(float(ts2) * (h @ w2_8.T))
+
+
+def _ffn_w4a8_no_ts2(x, w13_8, ts13, w2_8, ts2):
+    return _orig["swiglu_ffn_w4a8"](x, w13_8, ts13, w2_8, 1.0)
+
+
+def _layer_w4a8_as_w4a16(inp, tokens=None, logits=None):  # the FP8 steps left out
+    return _orig["layer"](inp, tokens=tokens, logits=logits)
+
+
+def _layer_w4a8_shared_dropped(inp, tokens=None, logits=None):
+    return _orig["layer_w4a8"](_no_shared(inp), tokens, logits)
+
+
 MUTANTS = {
     "bf16_round": [_bf16_truncate],
     "e2m1_value": [_e2m1_bias0],
@@ -192,6 +262,12 @@ MUTANTS = {
     "group_rmsnorm": [_group_norm_whole_row, _group_norm_no_eps, _group_norm_gamma_per_group],
     "add_rmsnorm": [_add_norm_of_x, _add_norm_no_residual],
     "layer": [_layer_shared_dropped, _layer_shared_gated, _layer_shared_wrong_rows, _layer_shared_up_as_gate],
+    "e4m3_round": [_e4m3_truncate, _e4m3_no_saturation, _e4m3_fnuz_subnormals],
+    "mxfp8_quantize": [_mx_scale_saturating, _mx_block16],
+    "dequant_e4m3": [_dequant_e4m3_unrounded],
+    "swiglu_hidden_w4a8": [_hidden_w4a8_unquantized, _hidden_w4a8_no_tscale],
+    "swiglu_ffn_w4a8": [_ffn_w4a8_h_unquantized, _ffn_w4a8_no_ts2],
+    "layer_w4a8": [_layer_w4a8_as_w4a16, _layer_w4a8_shared_dropped],
 }
 
 CASES = [(name, fn) for name, fns in MUTANTS.items() for fn in fns]

@@ -483,3 +483,189 @@ def test_layer_with_shared_expert_matches_torch_composition():
     sub = oracle.layer(inp, tokens=np.array([5, 1]))
     np.testing.assert_allclose(sub["o"], o.numpy()[[5, 1]], rtol=1e-12, atol=1e-10)
     np.testing.assert_allclose(sub["n"], n.numpy()[[5, 1]], rtol=1e-12, atol=1e-10)
+
+
+# ----------------------------------------------------------------------------
+# FP8 (W4A8) variant: E4M3 rounding, block-scaled activations, the FFN
+# ----------------------------------------------------------------------------
+def _e4m3_grid():
+    """Every finite non-negative E4M3FN value, from its bit fields (closed form)."""
+    vals = []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue  # NaN
+            vals.append(Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7))
+    return sorted(set(vals))
+
+
+def _nearest_even(v, grid):
+    """Nearest grid value to the rational v (ties -> even mantissa code), saturating."""
+    a = abs(v)
+    if a >= grid[-1]:
+        return grid[-1] * (1 if v >= 0 else -1)
+    import bisect
+    i = bisect.bisect_left(grid, a)
+    if grid[i] == a:
+        r = a
+    else:
+        lo, hi = grid[i - 1], grid[i]
+        if a - lo < hi - a:
+            r = lo
+        elif hi - a < a - lo:
+            r = hi
+        else:  # tie: the one whose mantissa code is even (its index in the grid is even)
+            r = lo if (i - 1) % 2 == 0 else hi
+    return r if v >= 0 else -r
+
+
+def test_e4m3_round_matches_brute_force_grid():
+    grid = _e4m3_grid()
+    assert len(grid) == 127 and grid[-1] == 448 and grid[1] == Fraction(1, 512)
+    rng = np.random.default_rng(31)
+    vals = np.concatenate([rng.standard_normal(300) * np.exp2(rng.uniform(-12, 10, 300)),
+                           [0.0, 448.0, -448.0, 464.0, 480.0, 1e9, 2.0 ** -10, 3 * 2.0 ** -11, 1.0625, 1.1875]])
+    got = oracle.e4m3_round(vals)
+    for v, g in zip(vals, got):
+        assert Fraction(g) == _nearest_even(Fraction(v), grid), v
+
+
+def test_e4m3_round_matches_torch_float8_in_range():
+    rng = np.random.default_rng(32)
+    v = (rng.standard_normal(5000) * np.exp2(rng.uniform(-11, 8, 5000))).astype(np.float32).astype(np.float64)
+    v = v[np.abs(v) < 440]
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.e4m3_round(v), ref)
+
+
+def test_mxfp8_quantize_block_scale_and_rounding():
+    rng = np.random.default_rng(33)
+    grid = _e4m3_grid()
+    x = rng.standard_normal((6, 96)) * np.exp2(rng.uniform(-20, 20, (6, 1)))
+    x[0, :32] = 0.0                                    # an all-zero block
+    x[1, :64] = 0.0
+    x[1, 5] = 1.75 * 2.0 ** 3                           # amax with mantissa exactly 1.75
+    x[1, 6] = -0.3
+    x[1, 40] = 1.875 * 2.0 ** -2                        # just above 1.75
+    x[1, 41] = 2.0 ** -12
+    q, e = oracle.mxfp8_quantize(x)
+    assert q.shape == x.shape and e.shape == (6, 3)
+    assert e[0, 0] == 0 and np.all(q[0, :32] == 0)
+    assert e[1, 0] == 3 - 8                             # 1.75 * 2^8 = 448 fits
+    assert e[1, 1] == -2 - 7                            # 1.875 * 2^8 > 448: one more
+    amax = np.max(np.abs(x.reshape(6, 3, 32)), axis=-1)
+    nz = amax > 0
+    assert np.all(amax[nz] * np.exp2(-e[nz]) <= 448)    # fits without saturating ...
+    assert np.all(amax[nz] * np.exp2(-(e[nz] - 1)) > 448)  # ... and e is the smallest that does
+    for r in range(6):
+        for c in range(96):
+            s = Fraction(2) ** int(e[r, c // 32])
+            assert Fraction(q[r, c]) == _nearest_even(Fraction(x[r, c]) / s, grid)
+
+
+def test_w4a8_reduces_to_w4a16_on_fp8_exact_inputs():
+    """With integer activations in [-4, 4] (exact in E4M3 after any power-of-two block
+    scale) and power-of-two weight scales 2^-4..2^0 (code * scale then has at most 2
+    significant bits, exact in E4M3), the FP8 up projection equals the W4A16 one, and
+    the FP8 FFN equals the W4A16 down projection of MXFP8(BF16(h))."""
+    rng = np.random.default_rng(34)
+    R, H, I = 5, 64, 64
+    x = rng.integers(-4, 5, (R, H)).astype(np.float64)
+    codes13 = rng.integers(0, 256, (2 * I, H // 2)).astype(np.uint8)
+    sc13 = wl.to_e4m3_codes(np.exp2(rng.integers(-4, 1, (2 * I, H // 16)).astype(np.float64)))
+    codes2 = rng.integers(0, 256, (H, I // 2)).astype(np.uint8)
+    sc2 = wl.to_e4m3_codes(np.exp2(rng.integers(-4, 1, (H, I // 16)).astype(np.float64)))
+    W13, W2 = oracle.dequant(codes13, sc13, 1.0), oracle.dequant(codes2, sc2, 1.0)
+    W13_8, W2_8 = oracle.dequant_e4m3(codes13, sc13), oracle.dequant_e4m3(codes2, sc2)
+    np.testing.assert_array_equal(W13_8, W13)
+    np.testing.assert_array_equal(W2_8, W2)
+    np.testing.assert_allclose(oracle.swiglu_hidden_w4a8(x, W13_8, 0.5), oracle.swiglu_hidden(x, W13 * 0.5),
+                               rtol=1e-13)
+    h = oracle.bf16_round(oracle.swiglu_hidden(x, W13))
+    q, e = oracle.mxfp8_quantize(h)
+    hq = q * np.repeat(np.exp2(e), 32, axis=1)
+    np.testing.assert_allclose(oracle.swiglu_ffn_w4a8(x, W13_8, 1.0, W2_8, 2.0),
+                               oracle.bf16_round(2.0 * hq @ W2.T), rtol=1e-13)
+
+
+def test_w4a8_ffn_brute_force():
+    """The FP8 FFN on a tiny shape against pure-Python loops: block scales by search
+    over the grid, exact rational products, math.fsum."""
+    rng = np.random.default_rng(35)
+    R, H, I = 2, 32, 32
+    grid = _e4m3_grid()
+    x = oracle.bf16_value(wl.to_bf16_bits(rng.standard_normal((R, H))))
+    codes13 = rng.integers(0, 256, (2 * I, H // 2)).astype(np.uint8)
+    sc13 = wl.to_e4m3_codes(np.exp2(rng.uniform(-4, 2, (2 * I, H // 16))))
+    codes2 = rng.integers(0, 256, (H, I // 2)).astype(np.uint8)
+    sc2 = wl.to_e4m3_codes(np.exp2(rng.uniform(-4, 2, (H, I // 16))))
+    W13 = oracle.dequant(codes13, sc13, 1.0)
+    W2 = oracle.dequant(codes2, sc2, 1.0)
+    w8 = lambda W: [[float(_nearest_even(Fraction(v), grid)) for v in row] for row in W]
+    W13_8, W2_8 = w8(W13), w8(W2)
+
+    def mx(row):  # one block of 32
+        amax = max(abs(Fraction(v)) for v in row)
+        if amax == 0:
+            return [0.0] * len(row)
+        e = -130
+        while amax / Fraction(2) ** e > 448:
+            e += 1
+        return [float(_nearest_even(Fraction(v) / Fraction(2) ** e, grid) * Fraction(2) ** e) for v in row]
+
+    got = oracle.swiglu_ffn_w4a8(x, np.array(W13_8), 1.0, np.array(W2_8), 1.0)
+    for r in range(R):
+        xq = mx(list(x[r]))
+        hrow = []
+        for i in range(I):
+            g = math.fsum(xq[c] * W13_8[i][c] for c in range(H))
+            u = math.fsum(xq[c] * W13_8[I + i][c] for c in range(H))
+            hrow.append(float(oracle.bf16_round(np.array(g / (1.0 + math.exp(-g)) * u))))
+        hq = mx(hrow)
+        for n in range(H):
+            want = float(oracle.bf16_round(np.array(math.fsum(hq[i] * W2_8[n][i] for i in range(I)))))
+            ulp = 2.0 ** (math.floor(math.log2(abs(want))) - 7) if want else 0.0
+            assert abs(got[r, n] - want) <= ulp, (r, n, got[r, n], want)
+
+
+def test_dequant_e4m3_rounds_each_weight():
+    rng = np.random.default_rng(36)
+    grid = _e4m3_grid()
+    codes = rng.integers(0, 256, (8, 16)).astype(np.uint8)
+    sc = wl.to_e4m3_codes(np.exp2(rng.uniform(-9, 8.7, (8, 2))))
+    got = oracle.dequant_e4m3(codes, sc)
+    exact = oracle.dequant(codes, sc, 1.0)
+    assert np.any(got != exact)                          # 6-bit products do get rounded
+    for r in range(8):
+        for c in range(32):
+            assert Fraction(got[r, c]) == _nearest_even(Fraction(exact[r, c]), grid)
+
+
+def test_layer_w4a8_matches_torch_composition():
+    """The FP8 layer, composed independently: torch.topk + torch.softmax routing, a
+    per-token loop over the selected experts' FP8 FFNs (swiglu_ffn_w4a8, pinned by brute
+    force above), the shared expert's FP8 FFN with weight 1, the residual, torch
+    rms_norm."""
+    w = wl.Workload("w4a8_pin", T=5, H=128, E=6, k=2, I=128, routing="normal", n_shared=1)
+    inp = wl.make_inputs(w, seed=23)
+    out = oracle.layer_w4a8(inp)
+    val = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double()
+    x, r, g = val(inp.x), val(inp.residual), val(inp.gamma)
+    L = torch.from_numpy(inp.logits.astype(np.float64))
+    sel = torch.topk(L, w.k, dim=1)
+    p = torch.softmax(L, dim=1).gather(1, sel.indices)
+    p = p / p.sum(dim=1, keepdim=True)
+    ffn = lambda xr, m13, m2, e: oracle.swiglu_ffn_w4a8(
+        xr, oracle.dequant_e4m3(m13.packed[e], m13.scales[e]), m13.tscale[e],
+        oracle.dequant_e4m3(m2.packed[e], m2.scales[e]), m2.tscale[e])
+    o = r.clone()
+    for t in range(w.T):
+        for j in range(w.k):
+            o[t] += p[t, j] * torch.from_numpy(ffn(x[t:t + 1].numpy(), inp.w13, inp.w2, int(sel.indices[t, j]))[0])
+    o += torch.from_numpy(ffn(x.numpy(), inp.shared13, inp.shared2, 0))
+    n = torch.nn.functional.rms_norm(o, (w.H,), weight=g, eps=w.eps)
+    assert np.array_equal(out["idx"], sel.indices.numpy())
+    np.testing.assert_allclose(out["o"], o.numpy(), rtol=1e-12, atol=1e-10)
+    np.testing.assert_allclose(out["n"], n.numpy(), rtol=1e-12, atol=1e-10)
+    # the FP8 layer is not the W4A16 one (the quantisation shows at the sampled size)
+    assert not np.allclose(out["o"], oracle.layer(inp)["o"], rtol=1e-6)

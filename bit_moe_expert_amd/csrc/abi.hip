@@ -59,9 +59,10 @@ moe4_status check_w4(const moe4_w4* w, const char* name) {
   NEED(w->packed, buf);
   snprintf(buf, sizeof(buf), "%s.scales", name);
   if (w->scales == nullptr) return fail(MOE4_ERR_INVALID_ARG, "%s is NULL", buf);
-  // scale rows are K/16 bytes: 8-byte multiples for K % 128 == 0; need 2-byte alignment
-  if (reinterpret_cast<uintptr_t>(w->scales) & 1u)
-    return fail(MOE4_ERR_INVALID_ARG, "%s is not 2-byte aligned", buf);
+  // scale rows are K/16 bytes: 8-byte multiples for K % 128 == 0; the GEMM copies
+  // them a dword at a time
+  if (reinterpret_cast<uintptr_t>(w->scales) & 3u)
+    return fail(MOE4_ERR_INVALID_ARG, "%s is not 4-byte aligned", buf);
   snprintf(buf, sizeof(buf), "%s.tscale", name);
   if (w->tscale == nullptr) return fail(MOE4_ERR_INVALID_ARG, "%s is NULL", buf);
   if (reinterpret_cast<uintptr_t>(w->tscale) & 3u)

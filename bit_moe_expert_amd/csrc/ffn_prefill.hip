@@ -8,29 +8,33 @@
 // compute"). So the 4-bit weights are dequantised exactly into BF16 once per
 // workgroup tile and fed to BF16 MFMAs with FP32 accumulation.
 //
-// Tiling. A workgroup (8 waves, two per SIMD) computes a 256-row x 256-column output
-// tile of one expert over K in steps of 64; each wave owns 128 x 64 of it as 4 x 2
-// blocks of 32x32x16 MFMAs (on gfx950 this shape runs near the BF16 peak, while
-// 16x16x32 tops out near half of it). Two waves per SIMD let one wave's MFMAs run while
-// the other waits on LDS or does its share of the dequantisation (with one wave of
-// 128 x 128 per SIMD the same tile ran slower). For the up projection the 256 weight
-// rows are 128 gate rows and the matching 128 up rows, and each wave takes 32 of each,
-// so gate and up accumulators of the same h columns sit in the same lanes and SwiGLU
-// is applied in registers. An expert's last tile, when it has at most 192 (or 128)
-// rows, is computed by all eight waves as 96 x 64 (or 64 x 64) tiles, again two waves
-// per SIMD, and the activation rows past 192 (or 128) are neither loaded nor stored.
+// Tiling. A workgroup of 4 waves (one per SIMD) computes a 256-row x 256-column output
+// tile of one expert over K in steps of 64; each wave owns all 256 rows of 64 columns
+// as 8 x 2 blocks of 32x32x16 MFMAs (on gfx950 this shape runs near the BF16 peak,
+// while 16x16x32 tops out near half of it), with its 256 accumulators in the AGPRs.
+// Because a wave owns its 64 weight rows alone, each weight is read and dequantised
+// once per tile, by one wave, straight into its MFMA operand registers: the weights
+// never pass through a shared LDS tile. Only the activations are shared: each wave
+// reads every activation row from LDS, 32 KB a step for 64 x 16 x 256 x 2 MFMA flops,
+// half the LDS bytes per flop of 128 x 64 wave tiles that take both operands from LDS.
+// For the up projection the 64 weight rows are 32 gate rows and the matching 32 up
+// rows, so gate and up accumulators of the same h columns sit in the same lanes and
+// SwiGLU is applied in registers. An expert's last tile, when it has at most 192 (or
+// 128) rows, is computed as 6 x 2 (or 4 x 2) blocks a wave, and the activation rows
+// past 192 (or 128) are neither loaded nor computed.
 //
-// Pipeline. Activation rows (gathered through perm_src for the up projection) and
-// weight half-tiles (tiled layout: 512 contiguous bytes per 16-row block; canonical:
-// 16 rows of 32 bytes) are loaded
-// into one of two register sets two steps ahead of use; during step i's MFMAs, step
-// i+1's set is dequantised (code * E4M3 scale is exact in BF16) and written to the
-// other LDS buffer part by part, each part's registers then refilled with step i+3.
-// The weights are read through the caches: every M-tile of an expert reads the same
-// weight tiles, and the tile order keeps those workgroups on one XCD. One barrier
-// per step. Each 16-wide K substep reads its operand fragments from LDS while
-// the previous one's MFMAs run. LDS rows are XOR-swizzled in 16-byte chunks so that
-// both the MFMA operand reads and the stores spread over the banks.
+// Pipeline. Every load is a direct-to-LDS copy (global_load_lds), issued two K steps
+// ahead into a ring of three LDS slots: the activation rows of the tile (gathered
+// through perm_src for the up projection), 8 rows per instruction, and each wave's own
+// weight codes and scales (tiled layout: 512 contiguous bytes per 16-row block and
+// step; canonical: 16 rows of 32 bytes). With only such copies in flight the wait at
+// the top of a step can leave the next step's copies outstanding (s_waitcnt with a
+// count), then one barrier makes the step's slot visible and frees the slot read two
+// steps ago. Within a step each 16-wide K substep reads its activation fragments from
+// LDS and dequantises its weight fragments (code * E4M3 scale is exact in BF16) while
+// the previous substep's MFMAs run. LDS rows are XOR-swizzled in 16-byte chunks (the
+// copies place a row's chunks at swizzled positions) so that the fragment reads of 16
+// rows at a time spread over all banks.
 //
 // Scheduling. One grid covers (expert M-tile, N-tile) pairs up to a bound; each
 // workgroup counts the per-expert tiles from the offsets, which gives the number of
@@ -50,7 +54,8 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kTq = 192;  // rows of a three-quarter tile
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
+constexpr int kBWave = 2 * 1024 + 2 * 256;  // weight bytes one wave copies per K step
 constexpr int kXcds = 8;
 constexpr int kMaxExperts = 256;  // the ABI's bound on G
 
@@ -71,6 +76,13 @@ struct GemmArgs {
   int tiled;                // weights in the tiled layout, else canonical
 };
 
+// One wave's weight operands of a K step, read from its LDS slot: the 16 code bytes
+// of each of its two 32-row blocks and the dword holding their two E4M3 scales.
+struct WRaw {
+  u32x4 c[2];
+  uint32_t s[2];
+};
+
 // LDS tiles are [rows][64] BF16, 128 bytes a row; the 16-byte chunk c of row r is stored
 // at chunk c ^ swz_key(r). The key keeps both access shapes free of bank conflicts (as
 // measured on gfx950): a 128-bit read serves 16 lanes at a time over 256 bytes of banks,
@@ -86,8 +98,18 @@ __device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3)
 // canonical); a compile-time choice, so the tiled form's addressing stays shifts.
 template <bool kUp, bool kDense, bool kTiled>
 __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BN * BK];
+  // three activation buffers [256][64] BF16 (the ring of steps st, st+1, st+2) and a
+  // fourth one for the epilogue's staging; separate arrays, so that the compiler can
+  // tell a direct-to-LDS copy into one from reads of another
+  __shared__ __attribute__((aligned(16))) uint16_t lds0[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds1[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds2[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds3[BM * BK];
+  // weight ring: per slot and wave, two blocks' code bytes (1 KB each, lane order) and
+  // their scale dwords (256 B each)
+  __shared__ __attribute__((aligned(16))) uint8_t ldsb0[4 * kBWave];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsb1[4 * kBWave];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsb2[4 * kBWave];
   __shared__ int sched[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -219,113 +241,88 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
 
   const int K = a.K, NS = K / 128, NB = a.N / 16, nsteps = K / BK;
   const float ts = a.tscale[g];
+  const int r32 = lane & 31, hh = lane >> 5;  // MFMA operand row / column; K half
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
-  // ---- global -> register loads ----
-  // A: thread t loads rows t/8 + 64i (i = 0..3), 16-byte chunk t%8 of the step. Rows
-  // past the tile's end read the tile's first row instead: their results are never
-  // stored, so they need no masking.
-  const int a_chunk = tid & 7;
-  const uint16_t* a_src[4];
+  // ---- weights: this wave's 64 B rows, straight from memory into registers ----
+  // Block j (0, 1) is 32 weight rows: up = gate rows 128nt + 32w .. +31 (j = 0) and the
+  // matching up rows (j = 1), so gate and up accumulators of one h column sit in the
+  // same lane; down = rows 256nt + 64w + 32j .. +31. In a K step (64 columns) lane l
+  // takes row l%32 of the block and the 32 columns 32hh .. 32hh+31 of the step: 16 code
+  // bytes and the 2 scale bytes of those columns. (The MFMA only needs A and B to agree
+  // on which K each lane group and slot stands for: in substep s lane group hh takes
+  // K = 32hh + 8s .. +7 of the step, in A as well.)
+  const uint8_t* bcode[2];
+  const uint8_t* bscale[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rr = (tid >> 3) + 64 * i;
-    int src = row0 + (rr < rows ? rr : 0);
-    if (kUp && !kDense) src = a.perm_src[src] / a.k;
-    a_src[i] = a.act + (size_t)src * K + a_chunk * 8;
-  }
-  // B: unit u = tid: 16-row block u/32, lane-in-half-tile u%32 (row rn = u%16 of the
-  // block, columns 32kq'..32kq'+31 of each 64-column step, kq' = (u%32)/16). Both
-  // layouts keep a block's codes (16 * K/2 bytes) and scales (16 * K/16) in one range
-  // at the same place; step st's 16 code bytes and 2 scale bytes of the unit sit at
-  // st * step + unit offset: tiled, 512 + 64 bytes a step (half a 16 x 128 tile) in
-  // lane order; canonical, 32 code bytes and 4 scale bytes a step along row rn.
-  const uint8_t* b_code[1];
-  const uint8_t* b_scale[1];
-  int b_st[1];  // LDS element offset of the unit's row (its 4 chunks are 4*kq' + j)
-  constexpr int bc_step = kTiled ? 512 : 32, bs_step = kTiled ? 64 : 4;
-#pragma unroll
-  for (int h = 0; h < 1; ++h) {
-    const int u = tid;
-    const int blk = u >> 5, l = u & 31;
-    int wblk;  // weight row-block of this LDS block
-    if (kUp) wblk = blk < 8 ? (nt * 128) / 16 + blk : (a.I + nt * 128) / 16 + (blk - 8);
-    else wblk = (nt * BN) / 16 + blk;
-    const size_t tile = ((size_t)g * NB + wblk) * NS;
-    const int rn = l & 15, kq = l >> 4;
-    b_code[h] = a.tcodes + tile * 1024 + (kTiled ? l * 16 : rn * (K / 2) + kq * 16);
-    b_scale[h] = a.tscales + tile * 128 + (kTiled ? l * 2 : rn * (K / 16) + kq * 2);
-    b_st[h] = blk * 16 + (l & 15);
-  }
-  const int b_kq = (tid & 31) >> 4;  // same for both units
-  // LDS swizzle (swz_key): for every row a lane touches, the key depends only on the
-  // lane (row offsets are multiples of 16), so the addresses are a
-  // per-lane base plus immediate offsets.
-  const int a_sw = swz_key(tid >> 3);
-  const int a_st = (tid >> 3) * BK + ((a_chunk ^ a_sw) << 3);  // + 64*i*BK for row group i
-  const int b_sw = swz_key(tid & 15);
-
-  // Two register sets, used by alternate steps: step s's data is loaded during step
-  // s - 2 and written to LDS during step s - 1, so every load has a whole step and more
-  // to arrive.
-  u32x4 ra[2][4], rb[2];
-  uint32_t rs[2];
-  // Part q of step st's global loads into set S: activation row q of this thread and,
-  // for q = 3, the weight unit (whose four store parts have then all been written).
-  // (groups: the activation row groups of 64 the tile needs, 4, 3 or 2)
-  auto load_part = [&](auto SET, int st, int q, int groups) {
-    constexpr int S = decltype(SET)::value;
-    const int k0 = st * BK;
-    if (q < groups) ra[S][q] = *reinterpret_cast<const u32x4*>(a_src[q] + k0);
-    if (q == 3) {
-      // (tiled: st * 512 and st * 64, written per 1 KB tile and half, which the
-      // compiler turns into fewer live registers than the product)
-      const size_t toff = kTiled ? (size_t)(st >> 1) * 1024 + (st & 1) * 512 : (size_t)st * bc_step;
-      const size_t soff = kTiled ? (size_t)(st >> 1) * 128 + (st & 1) * 64 : (size_t)st * bs_step;
-      rb[S] = *reinterpret_cast<const u32x4*>(b_code[0] + toff);
-      rs[S] = *reinterpret_cast<const uint16_t*>(b_scale[0] + soff);
+  for (int j = 0; j < 2; ++j) {
+    const int n0 = kUp ? (j == 0 ? nt * 128 + 32 * wv : a.I + nt * 128 + 32 * wv) : nt * BN + 64 * wv + 32 * j;
+    const int row = n0 + r32;
+    if constexpr (kTiled) {
+      // tile (g, row/16, kt): lane rn + 16 kq of it, kq = 2 (st % 2) + hh
+      const size_t tile = ((size_t)g * NB + row / 16) * NS;
+      bcode[j] = a.tcodes + tile * 1024 + ((row & 15) + 16 * hh) * 16;
+      bscale[j] = a.tscales + tile * 128 + ((row & 15) + 16 * hh) * 2;
+    } else {
+      const size_t r = (size_t)g * a.N + row;
+      bcode[j] = a.tcodes + r * (K / 2) + hh * 16;
+      bscale[j] = a.tscales + r * (K / 16) + hh * 2;
     }
-  };
-  // Part q (0..3) of writing set S into LDS buffer `buf`: activation row q of this
-  // thread, and BF16 chunk q of the weight unit (dequantised here).
-  auto store_part = [&](auto SET, int buf, int q, int groups) {
-    constexpr int S = decltype(SET)::value;
-    if (q < groups) *reinterpret_cast<u32x4*>(&lds_a[buf][a_st + 64 * q * BK]) = ra[S][q];
-    const float sc = q < 2 ? e4m3_to_f32<0>(rs[S]) : e4m3_to_f32<1>(rs[S]);
-    *reinterpret_cast<u32x4*>(&lds_b[buf][b_st[0] * BK + (((4 * b_kq + q) ^ b_sw) << 3)]) = dequant8(rb[S][q], sc);
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-
-  // ---- per-wave tile: 128 rows x 64 LDS B rows as 4 x 2 blocks of 32x32x16 MFMAs ----
-  // An expert's last tile of at most 192 rows (three-quarter) or 128 rows (half) is
-  // computed by all eight waves as 96- or 64-row x 64 tiles (3 x 2 or 2 x 2 blocks),
-  // two waves per SIMD as in a full tile; the activation rows past 192 or 128 are
-  // neither loaded nor stored. Each output is the same chain of MFMAs over K in every
-  // tile shape, so the shape does not change any bits.
-  const int wm = wave >> 2, wn = wave & 3;
-  const int r32 = lane & 31, kh = lane >> 5;  // operand row within a 32-block; K half (8 values)
-  // LDS B rows of block j: up = gate rows 64wn + 32j (j < 2) then up rows
-  // 128 + 64wn + 32(j-2); down = rows 128wn + 32j. Row offsets are multiples of 32.
-  int boff[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) boff[j] = kUp ? 128 * j + 32 * wn : 64 * wn + 32 * j;
-  const int f_sw = swz_key(r32);
-  const int fb_base = r32 * BK;
+  }
 
   auto compute = [&](auto MIC) {
-    constexpr int MI = decltype(MIC)::value;  // 32-row blocks of a wave's tile: 4, 3 or 2
-    // Prologue: step 0 into LDS buffer 0, steps 1 and 2 into register sets 1 and 0.
+    constexpr int MI = decltype(MIC)::value;  // 32-row blocks of the tile: 8, 6 or 4
+    constexpr int RW = 8 * MI;                // activation rows each wave copies
+    // ---- activations: rows of the tile straight into LDS (global_load_lds) ----
+    // Wave w copies LDS rows RW*w .. RW*w + RW-1, 8 rows (1 KB) per instruction: lane l
+    // fills row RW*w + 8i + l/8, 16-byte position l%8, with the row's global chunk
+    // (l%8) ^ swz_key(row), so that chunk c of row r sits at position c ^ swz_key(r).
+    // Rows past the tile's end copy its first row: their results are never stored.
+    // (sized 8, the most MI, rather than MI: passing an element of an array sized by
+    // the lambda's template value to the copy builtin made hipcc's host pass drop the
+    // kernel's launch stubs)
+    const uint16_t* asrc[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load_part(S0{}, 0, q, MI);
+    for (int i = 0; i < MI; ++i) {
+      const int rr = RW * wv + 8 * i + (lane >> 3);
+      int src = row0 + (rr < rows ? rr : 0);
+      if (kUp && !kDense) src = a.perm_src[src] / a.k;
+      asrc[i] = a.act + (size_t)src * K + (((lane & 7) ^ swz_key(rr)) << 3);
+    }
+    auto buf_of = [&](auto RC) -> uint16_t* {
+      constexpr int R = decltype(RC)::value;
+      return R == 0 ? lds0 : (R == 1 ? lds1 : lds2);
+    };
+    auto load_a = [&](int st, uint16_t* b) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) store_part(S0{}, 0, q, MI);
+      for (int i = 0; i < MI; ++i)
+        __builtin_amdgcn_global_load_lds(asrc[i] + st * BK,
+                                         (__attribute__((address_space(3))) void*)&b[(RW * wv + 8 * i) * BK],
+                                         16, 0, 0);
+    };
+    // weights: also straight into LDS (this wave's own region of the slot), so that
+    // every load in flight is a direct-to-LDS copy and the waits on them can be counted
+    auto bbuf_of = [&](auto RC) -> uint8_t* {
+      constexpr int R = decltype(RC)::value;
+      return (R == 0 ? ldsb0 : (R == 1 ? ldsb1 : ldsb2)) + wv * kBWave;
+    };
+    auto load_b = [&](int st, uint8_t* b) {
+      // step st's offsets from the bases (tiled: 1 KB + 128 B per 128-column tile, half
+      // of it per step; canonical: 32 + 4 bytes per step along the row)
+      const size_t co = kTiled ? (size_t)(st >> 1) * 1024 + (st & 1) * 512 : (size_t)st * 32;
+      const size_t so = kTiled ? (size_t)(st >> 1) * 128 + (st & 1) * 64 : (size_t)st * 4;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load_part(S1{}, min(1, nsteps - 1), q, MI);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) load_part(S0{}, min(2, nsteps - 1), q, MI);
-    __syncthreads();
-    constexpr int WR = 32 * MI;        // rows of a wave's tile
-    const int fa_base = (WR * wm + r32) * BK;
+      for (int j = 0; j < 2; ++j) {
+        const uint8_t* cp = bcode[j] + co;
+        // the dword holding this lane's 2 scale bytes
+        const uint8_t* sp = bscale[j] + so;
+        const uint8_t* sd = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(sp) & ~uintptr_t(3));
+        __builtin_amdgcn_global_load_lds(cp, (__attribute__((address_space(3))) void*)(b + j * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(sd, (__attribute__((address_space(3))) void*)(b + 2048 + j * 256), 4, 0, 0);
+      }
+    };
+    // this lane's two 16-bit scale pairs sit in the upper or lower half of its dword
+    const int sc_shift = (int)((reinterpret_cast<uintptr_t>(bscale[0]) & 2) * 8);
     f32x16 acc[MI][2];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -334,60 +331,152 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // operand fragments of one 16-wide K substep
-    u32x4 fa[MI], fb[2], na[MI], nb[2];
-    auto read_frags = [&](int buf, int ks, u32x4* A, u32x4* Bv) {
-      const int cs = ((2 * ks + kh) ^ f_sw) << 3;
+    const int key = swz_key(r32);
+    auto read_a = [&](auto RC, int s, u32x4* A) {
+      const uint16_t* b = buf_of(RC);
+      const int cs = ((4 * hh + s) ^ key) << 3;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) Bv[j] = *reinterpret_cast<const u32x4*>(&lds_b[buf][fb_base + boff[j] * BK + cs]);
-#pragma unroll
-      for (int i = 0; i < MI; ++i) A[i] = *reinterpret_cast<const u32x4*>(&lds_a[buf][fa_base + 32 * i * BK + cs]);
+      for (int i = 0; i < MI; ++i) A[i] = *reinterpret_cast<const u32x4*>(&b[(32 * i + r32) * BK + cs]);
     };
-    read_frags(0, 0, fa, fb);
-    // Steps come in pairs (K is a multiple of 128): step st writes set (st + 1) % 2.
-    auto step = [&](auto SET, int st) {
-      const int buf = st & 1;
-      const int next3 = min(st + 3, nsteps - 1);  // the last steps reload themselves (never read)
-      // Four 16-wide substeps. In each, the next substep's fragments are read while this
-      // one's MFMAs run; then one part of step st+1 is written to the other buffer, and
-      // its registers are refilled with step st+3.
+    auto read_b = [&](auto RC, WRaw& r) {
+      const uint8_t* b = bbuf_of(RC);
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        if (ks + 1 < BK / 16) read_frags(buf, ks + 1, na, nb);
+      for (int j = 0; j < 2; ++j) {
+        r.c[j] = *reinterpret_cast<const u32x4*>(b + j * 1024 + lane * 16);
+        r.s[j] = *reinterpret_cast<const uint32_t*>(b + 2048 + j * 256 + lane * 4) >> sc_shift;
+      }
+    };
+    auto deq_b = [&](const WRaw& r, int s, u32x4* Bv) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float sc = s < 2 ? e4m3_to_f32<0>(r.s[j]) : e4m3_to_f32<1>(r.s[j]);
+        Bv[j] = dequant8(r.c[j][s], sc);
+      }
+    };
+    // s_waitcnt vmcnt(MI + 4) lgkmcnt(0): at most one step's copies (MI activation
+    // copies, 4 weight copies) still in flight, every LDS read of this wave done
+    // (gfx9 encoding, expcnt left at its maximum)
+    constexpr int kAfter = MI + 4;
+    constexpr int kWait = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (0 << 8);
+
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    // The operands of the next MFMA substep, carried across steps: the last substep of
+    // step st reads step st+1's first fragments.
+    WRaw raw;
+    u32x4 fa[MI], fb[2];
+    // Prologue: steps 0 and 1 in flight; step 0 landed everywhere; its first operands.
+    load_a(0, buf_of(C0{}));
+    load_b(0, bbuf_of(C0{}));
+    load_a(min(1, nsteps - 1), buf_of(C1{}));
+    load_b(min(1, nsteps - 1), bbuf_of(C1{}));
+    __builtin_amdgcn_s_waitcnt(kWait);
+    asm volatile("s_barrier" ::: "memory");
+    read_b(C0{}, raw);
+    read_a(C0{}, 0, fa);
+    deq_b(raw, 0, fb);
+    // One K step from ring slot R (= st % 3, a compile-time index). Its substep 0
+    // operands are in fa / fb. One barrier a step, before the last substep: by then
+    // every wave has read all of step st but the last substep's fragments (which it
+    // holds), so the slot of step st-1 is free for the copies of step st+2 issued at
+    // the next step's start, and every wave's copies of step st+1 have landed, so the
+    // last substep can fetch step st+1's first operands under its MFMAs. (A bare
+    // s_barrier: a workgroup fence would also wait for the copies of step st+2, which
+    // are in flight on purpose.)
+    auto step = [&](auto RC, int st) {
+      constexpr int R = decltype(RC)::value;
+      constexpr int R1 = (R + 1) % 3, R2 = (R + 2) % 3;
+      using CR1 = std::integral_constant<int, R1>;
+      using CR2 = std::integral_constant<int, R2>;
+      const int nx = min(st + 2, nsteps - 1);  // the last steps reload themselves (never read)
+      u32x4 na[MI], nb[2];
+      WRaw raw_next;
+#pragma unroll
+      for (int s = 0; s < BK / 16; ++s) {
+        if (s == BK / 16 - 1) {
+          __builtin_amdgcn_s_waitcnt(kWait);
+          asm volatile("s_barrier" ::: "memory");
+        }
+        // One wave per SIMD hides nothing by itself: the next substep's fragment reads
+        // and dequantisation (and in substep 0 the copies of step st+2) are spread
+        // between this substep's MFMAs, so the MFMA pipe never waits on them.
+        if (s == 0) {
+          load_a(nx, buf_of(CR2{}));
+          load_b(nx, bbuf_of(CR2{}));
+        }
+        if (s + 1 < BK / 16) {
+          read_a(RC, s + 1, na);
+          deq_b(raw, s + 1, nb);
+        } else {
+          read_b(CR1{}, raw_next);
+          read_a(CR1{}, 0, na);
+          deq_b(raw_next, 0, nb);
+        }
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
-        store_part(SET, buf ^ 1, ks, MI);
-        load_part(SET, next3, ks, MI);
-        if (ks + 1 < BK / 16) {
+        if (s + 1 < BK / 16) {
 #pragma unroll
-          for (int i = 0; i < MI; ++i) fa[i] = na[i];
+          for (int g2 = 0; g2 < MI; ++g2) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM (copies)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+          }
+        } else {
+          // the next step's reads first (the weight bytes, whose dequantisation waits
+          // for them, then the activation fragments), the dequantisation after them
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) fb[j] = nb[j];
+          for (int g2 = 0; g2 < MI / 2; ++g2) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+#pragma unroll
+          for (int g2 = 0; g2 < 2 * MI - 1 - MI / 2; ++g2) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) fa[i] = na[i];
+        fb[0] = nb[0];
+        fb[1] = nb[1];
       }
-      __syncthreads();
-      read_frags(buf ^ 1, 0, fa, fb);
+      raw = raw_next;
     };
-    for (int st = 0; st < nsteps; st += 2) {
-      step(S1{}, st);
-      step(S0{}, st + 1);
+    // The loop body runs whole rounds of the ring, with no branch inside, so that the
+    // compiler's own waits see the same loads in flight on every path; the steps past
+    // the last whole round follow it.
+    int st = 0;
+    for (const int st_end = nsteps - nsteps % 3; st < st_end; st += 3) {
+      step(C0{}, st);
+      step(C1{}, st + 1);
+      step(C2{}, st + 2);
     }
+    if (st < nsteps) step(C0{}, st);
+    if (st + 1 < nsteps) step(C1{}, st + 1);
+    // every load issued has landed before the LDS is reused (the last ones are reloads)
+    __builtin_amdgcn_s_waitcnt(0);
 
-    // ---- epilogue: acc[i][j][r] is row 8(r/4) + 4kh + r%4, column r32 of block (i, j) ----
-    // The wave's outputs go through LDS (the operand buffers are free once every wave
-    // has passed the barrier), so that each lane writes whole 16-byte row pieces: 8 (up)
-    // or 16 (down) stores a wave instead of 64 or 128 of 2 bytes. A wave's LDS region is
-    // its own [WR][W] BF16 block (W = 32 h columns for up, 64 y columns for down).
+    // ---- epilogue: acc[i][j][r] is row 32i + 8(r/4) + 4hh + r%4, column r32 of block j ----
+    // The wave's outputs go through LDS (its own [256][W] BF16 region: W = 32 h columns
+    // for up, 64 y columns for down) so that each lane writes whole 16-byte row pieces.
     __syncthreads();
     constexpr int W = kUp ? 32 : 64;
-    uint16_t* stage = (wave < 4 ? &lds_a[0][0] : &lds_b[0][0]) + (wave & 3) * (128 * W);
+    // (wave w's region: the first W * 256 elements of buffer w; buffers are 256 x 64)
+    uint16_t* stage = (wv == 0 ? lds0 : wv == 1 ? lds1 : wv == 2 ? lds2 : lds3);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int lr = 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
+        const int lr = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
         if (kUp) {
           stage[lr * W + r32] = f32_to_bf16(silu_mul(ts * acc[i][0][r], ts * acc[i][1][r]));
         } else {
@@ -399,21 +488,20 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    constexpr int kPieces = WR * W / 8;  // 16-byte pieces of the wave's block
+    constexpr int kPieces = 32 * MI * W / 8;  // 16-byte pieces of the wave's block
     const size_t ld = kUp ? a.I : a.N;
-    const int col0 = kUp ? nt * 128 + 32 * wn : nt * BN + 64 * wn;
+    const int col0 = kUp ? nt * 128 + 32 * wv : nt * BN + 64 * wv;
 #pragma unroll
     for (int c = 0; c < kPieces / 64; ++c) {
       const int piece = 64 * c + lane, lr = piece / (W / 8), lc = (piece % (W / 8)) * 8;
-      const int tr = WR * wm + lr;
-      if (tr < rows)
-        *reinterpret_cast<u32x4*>(a.out + (size_t)(row0 + tr) * ld + col0 + lc) =
+      if (lr < rows)
+        *reinterpret_cast<u32x4*>(a.out + (size_t)(row0 + lr) * ld + col0 + lc) =
             *reinterpret_cast<const u32x4*>(stage + lr * W + lc);
     }
   };
-  if (rows <= BM / 2) compute(std::integral_constant<int, 2>{});
-  else if (rows <= kTq) compute(std::integral_constant<int, 3>{});
-  else compute(std::integral_constant<int, 4>{});
+  if (rows <= BM / 2) compute(std::integral_constant<int, 4>{});
+  else if (rows <= kTq) compute(std::integral_constant<int, 6>{});
+  else compute(std::integral_constant<int, 8>{});
 }
 
 hipError_t launch(bool up, GemmArgs a, long long m_tiles, hipStream_t s) {

@@ -105,8 +105,7 @@ typedef enum {
 
 /* One grouped 4-bit weight tensor over G experts (host struct of device pointers).
  * packed: G*N*K/2 code bytes and scales: G*N*K/16 E4M3 bytes, both in `layout`;
- * tscale [G] FP32. packed is 16-byte aligned, scales 2-byte aligned, tscale 4-byte
- * aligned. */
+ * tscale [G] FP32. packed is 16-byte aligned, scales and tscale 4-byte aligned. */
 typedef struct {
   const uint8_t* packed;
   const uint8_t* scales;

@@ -98,6 +98,9 @@ def test_null_and_misaligned_pointers():
     assert lib.moe4_expert_ffn(s, FAKE, FAKE, None, w, w, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
     assert lib.moe4_expert_ffn(s, FAKE, FAKE, FAKE, w, nul, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
     assert b"w2.scales" in lib.moe4_last_error()
+    odd = W4(FAKE, FAKE + 2, FAKE, _lib.MOE4_W4_TILED)  # scales are read a dword at a time
+    assert lib.moe4_expert_ffn(s, FAKE, FAKE, FAKE, odd, w, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
+    assert b"w13.scales is not 4-byte aligned" in lib.moe4_last_error()
     assert lib.moe4_combine_norm(s, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None) == _lib.MOE4_ERR_INVALID_ARG
     assert b"gamma" in lib.moe4_last_error()
 

@@ -388,7 +388,11 @@ def dequant_e4m3(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """One expert's 4-bit matrix with each weight (code * E4M3 block scale, exact)
     rounded to E4M3 (reading R18) -> fp64 [N, K]; the tensor scale is left out (it
     multiplies the sums)."""
-    return e4m3_round(dequant(packed, scales, 1.0))
+    # the rounded product of every (code, scale) pair, taken once each (16 x 256)
+    table = e4m3_round(e2m1_value(np.arange(16))[:, None] * e4m3_value(np.arange(256))[None, :])
+    codes = unpack_codes(packed)
+    sc = np.repeat(np.asarray(scales, dtype=np.uint8), 16, axis=-1)
+    return table[codes, sc]
 
 
 def swiglu_hidden_w4a8(x: np.ndarray, w13_8: np.ndarray, tscale: float) -> np.ndarray:
@@ -411,7 +415,8 @@ def swiglu_ffn_w4a8(x, w13_8, ts13, w2_8, ts2) -> np.ndarray:
 def layer_w4a8(inp, tokens=None, logits=None):
     """The whole layer with the W4A8 FFN (reading R18) for the routed experts and the
     shared expert; routing, combine and norm as in ``layer``. Returns the same dict
-    (without the plan)."""
+    (without the plan), plus the BF16 h of every (token, slot) ("h", [T, k, I]) and of
+    the shared expert ("h_shared")."""
     wl = inp.w
     T = inp.x.shape[0]
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
@@ -421,15 +426,19 @@ def layer_w4a8(inp, tokens=None, logits=None):
     idx, w = route(logits, wl.k)
     x = bf16_value(np.asarray(inp.x)[tok])
     y = np.zeros((len(tok), wl.k, x.shape[1]), dtype=np.float64)
+    h = np.zeros((len(tok), wl.k, wl.I), dtype=np.float64)
     for e in np.unique(idx):
         rr, jj = np.nonzero(idx == e)
         W13 = dequant_e4m3(inp.w13.packed[e], inp.w13.scales[e])
         W2 = dequant_e4m3(inp.w2.packed[e], inp.w2.scales[e])
+        h[rr, jj] = bf16_round(swiglu_hidden_w4a8(x[rr], W13, inp.w13.tscale[e]))
         y[rr, jj] = swiglu_ffn_w4a8(x[rr], W13, inp.w13.tscale[e], W2, inp.w2.tscale[e])
-    shared = None
+    shared = h_shared = None
     if getattr(inp, "shared13", None) is not None:
         S13 = dequant_e4m3(inp.shared13.packed[0], inp.shared13.scales[0])
         S2 = dequant_e4m3(inp.shared2.packed[0], inp.shared2.scales[0])
+        h_shared = bf16_round(swiglu_hidden_w4a8(x, S13, inp.shared13.tscale[0]))
         shared = swiglu_ffn_w4a8(x, S13, inp.shared13.tscale[0], S2, inp.shared2.tscale[0])
     o, n = combine_norm(y, w, np.asarray(inp.residual)[tok], inp.gamma, wl.eps, shared)
-    return {"logits": logits, "idx": idx, "w": w, "y": y, "o": o, "n": n, "tokens": tok, "shared": shared}
+    return {"logits": logits, "idx": idx, "w": w, "y": y, "o": o, "n": n, "tokens": tok, "shared": shared,
+            "h": h, "h_shared": h_shared}

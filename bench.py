@@ -46,6 +46,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA TFLOP/s as % of peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 MALL_DEFEAT_BYTES = 1 << 30
 
 
@@ -64,6 +65,10 @@ def parse():
                     help="what a step is: the MoE layer (default), or one of the neighbouring "
                          "RMSNorm glue launches over the workload's T x H rows")
     ap.add_argument("--group", type=int, default=0, help="group_rmsnorm group size (0 = H / 8)")
+    ap.add_argument("--precision", choices=["w4a16", "w4a8"], default="w4a16",
+                    help="expert FFN form: BF16 activations (the default), or the FP8 prefill "
+                         "variant (moe4_layer_w4a8: block-scaled E4M3 activations, weights "
+                         "rounded to E4M3, FP8 MFMA)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB twice with torch (a plain copy of known size, for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -106,12 +111,13 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def ffn_work(w, T, idx, up, dense):
+def ffn_work(w, T, idx, up, dense, fp8=False):
     """Algorithmic bytes and flops of one expert-FFN launch: the routed groups of the
     plan (dense False; ``idx`` the routing) or the shared expert over all T tokens.
     Bytes: the touched experts' packed codes + E4M3 scales + tensor scale, the
     activations read (x once per token for up; h rows for down), the outputs written,
-    and the plan."""
+    and the plan. With ``fp8`` the activations in (and h out of up) are E4M3 codes
+    plus one scale byte per 32."""
     N, K = (2 * w.I, w.H) if up else (w.H, w.I)
     per_expert = N * K // 2 + N * K // 16 + 4
     if dense:
@@ -120,8 +126,9 @@ def ffn_work(w, T, idx, up, dense):
         rows = T * w.k
         experts = len(set(idx.reshape(-1).tolist()))
         plan = (w.E + 1) * 4 + (rows * 4 if up else 0)
-    act_in = T * w.H * 2 if up else rows * w.I * 2
-    out = rows * (w.I if up else w.H) * 2
+    a = 1 + 1 / 32 if fp8 else 2
+    act_in = int(T * w.H * a) if up else int(rows * w.I * a)
+    out = int(rows * w.I * a) if up else rows * w.H * 2
     nbytes = experts * per_expert + act_in + out + plan
     flops = 2 * rows * N * K
     return nbytes, flops, experts
@@ -137,20 +144,22 @@ def _oracle_worker(wid, calls, budget_s):
 
     import oracle
     inputs = _CPU["inputs"]
+    fn = oracle.layer_w4a8 if _CPU["fp8"] else oracle.layer
     done, t0 = 0, time.perf_counter()
     with threadpool_limits(limits=1):
         for chunk, tokens in calls:
-            oracle.layer(inputs[chunk], tokens=tokens)
+            fn(inputs[chunk], tokens=tokens)
             done += len(tokens)
             if time.perf_counter() - t0 >= budget_s:
                 break
     return done, time.perf_counter() - t0
 
 
-def cpu_baseline(inputs, budget_s):
+def cpu_baseline(inputs, budget_s, fp8=False):
     """Time the oracle as it stands on all host cores: one worker process per core
-    (forked before the GPU is initialised), each running oracle.layer on its own
-    seeded subsets of the workload's tokens, BLAS one thread per worker."""
+    (forked before the GPU is initialised), each running oracle.layer (with ``fp8``
+    oracle.layer_w4a8) on its own seeded subsets of the workload's tokens, BLAS one
+    thread per worker."""
     import multiprocessing
 
     import numpy as np
@@ -177,6 +186,7 @@ def cpu_baseline(inputs, budget_s):
             calls.append((c, np.unique(perms[c][np.arange(p, p + per_call) % T])))
         plans.append(calls)
     _CPU["inputs"] = inputs
+    _CPU["fp8"] = fp8
     ctx = multiprocessing.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(cores) as pool:
@@ -186,7 +196,8 @@ def cpu_baseline(inputs, budget_s):
     tokens = sum(r[0] for r in res)
     return {"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{tokens} token evaluations: seeded subsets of the {T * chunks}-token workload "
-                      f"(all chunks, cycling), oracle layer calls of up to {per_call} tokens on {cores} "
+                      f"(all chunks, cycling), oracle {'layer_w4a8' if fp8 else 'layer'} calls of up to "
+                      f"{per_call} tokens on {cores} "
                       f"worker processes (one per host core, BLAS 1 thread each), {wall:.1f} s wall"}
 
 
@@ -271,7 +282,7 @@ def glue_main(args):
     desc = f"group={G}" if not add else "o = x + residual"
     out = {"metric": f"{args.op} rows/s", "value": round(T / mean_s, 1), "unit": "rows/s", "n_gpus": 1,
            "steps": replays * per_graph, "warmup": args.warmup, "ms_per_step": round(mean_s * 1e3, 6),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8" if fp8 else "bf16",
            "data": "synthetic",
            "config": {"workload": f"{args.op} over {T} rows of H={H} BF16 ({desc}), rows of the "
                                   f"{args.config} workload; launches replayed from a HIP graph",
@@ -334,7 +345,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on every host core for ~{args.cpu_seconds:.0f} s")
-        cpu = cpu_baseline(inputs, args.cpu_seconds)
+        cpu = cpu_baseline(inputs, args.cpu_seconds, fp8=args.precision == "w4a8")
         log(f"cpu baseline: {cpu['value']:.2f} tokens/s on {cpu['cores']} cores")
 
     torch.cuda.set_device(0)
@@ -361,7 +372,15 @@ def main():
     topk_w = torch.empty((T, w.k), dtype=torch.float32, device="cuda")
     res_out = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
     norm_out = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
-    ws = torch.empty(B.moe4_layer_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    fp8 = args.precision == "w4a8"
+    ws_n = B.moe4_w4a8_workspace_bytes(shape) if fp8 else B.moe4_layer_workspace_bytes(shape)
+    if ws_n == 0:
+        print(f"bench.py: {args.config} is not a valid shape for --precision {args.precision}", file=sys.stderr)
+        sys.exit(2)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    if fp8 and args.side_stream == "on":
+        print("bench.py: --side-stream applies to the W4A16 layer only", file=sys.stderr)
+        sys.exit(2)
 
     use_side = args.side_stream == "on" and w.n_shared > 0
     side = torch.cuda.Stream() if use_side else None
@@ -371,8 +390,12 @@ def main():
     def layer_step(i):
         c = per_chunk[i % chunks]
         a13, a2 = weights[(i // chunks) % copies]
-        B.moe4_layer(shape, c["x"], wr, c["logits"], a13, a2, s13, s2, c["residual"], gamma, topk_idx,
-                     topk_w, res_out, norm_out, ws, side_stream=side)
+        if fp8:
+            B.moe4_layer_w4a8(shape, c["x"], wr, c["logits"], a13, a2, s13, s2, c["residual"], gamma, topk_idx,
+                              topk_w, res_out, norm_out, ws)
+        else:
+            B.moe4_layer(shape, c["x"], wr, c["logits"], a13, a2, s13, s2, c["residual"], gamma, topk_idx,
+                         topk_w, res_out, norm_out, ws, side_stream=side)
 
     stream = torch.cuda.current_stream()
     if args.copy_calibration:
@@ -424,44 +447,74 @@ def main():
     pws_n = B.moe4_permute_workspace_bytes(shape)
     pws = torch.empty(pws_n, dtype=torch.uint8, device="cuda") if pws_n else None
     plans, routing, hs, hds = [], [], [], []
+    u8 = lambda *shp: torch.empty(shp, dtype=torch.uint8, device="cuda")
+    # the FP8 form's halves take the activations already quantised (per chunk, once)
+    fp8_h = lambda rows: (u8(rows, w.I), u8(rows, w.I // 32))
     for c in per_chunk:
         offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
         perm_src = torch.empty(pairs, dtype=torch.int32, device="cuda")
         inv = torch.empty(pairs, dtype=torch.int32, device="cuda")
         B.moe4_route(shape, c["x"] if wr is not None else None, wr, c["logits"], topk_idx, topk_w)
         B.moe4_permute(shape, topk_idx, offsets, perm_src, inv, pws)
-        h = torch.empty((pairs, w.I), dtype=torch.int16, device="cuda")
-        B.moe4_expert_up(shape, c["x"], offsets, perm_src, w13, h)
+        if fp8:
+            c["x8"], c["xs"] = u8(T, w.H), u8(T, w.H // 32)
+            B.moe4_quant_mxfp8(c["x"], c["x8"], c["xs"])
+            h = fp8_h(pairs)
+            B.moe4_expert_up_w4a8(shape, c["x8"], c["xs"], offsets, perm_src, w13, None, *h)
+        else:
+            h = torch.empty((pairs, w.I), dtype=torch.int16, device="cuda")
+            B.moe4_expert_up(shape, c["x"], offsets, perm_src, w13, h)
         hs.append(h)
         if s13 is not None:
-            hd = torch.empty((T, w.I), dtype=torch.int16, device="cuda")
-            B.moe4_expert_up(shape, c["x"], None, None, s13, hd)
+            if fp8:
+                hd = fp8_h(T)
+                B.moe4_expert_up_w4a8(shape, c["x8"], c["xs"], None, None, s13, None, *hd)
+            else:
+                hd = torch.empty((T, w.I), dtype=torch.int16, device="cuda")
+                B.moe4_expert_up(shape, c["x"], None, None, s13, hd)
             hds.append(hd)
         torch.cuda.synchronize()
         routing.append(topk_idx.cpu().numpy())
         plans.append((offsets, perm_src))
     y = torch.empty((pairs, w.H), dtype=torch.int16, device="cuda")
     yd = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
-    h_tmp = torch.empty((pairs, w.I), dtype=torch.int16, device="cuda")
-    hd_tmp = torch.empty((T, w.I), dtype=torch.int16, device="cuda")
+    h_tmp = fp8_h(pairs) if fp8 else torch.empty((pairs, w.I), dtype=torch.int16, device="cuda")
+    hd_tmp = fp8_h(T) if fp8 else torch.empty((T, w.I), dtype=torch.int16, device="cuda")
 
     def up_routed(i):
         c = per_chunk[i % chunks]
         offsets, perm_src = plans[i % chunks]
-        B.moe4_expert_up(shape, c["x"], offsets, perm_src, weights[(i // chunks) % copies][0], h_tmp)
+        a13 = weights[(i // chunks) % copies][0]
+        if fp8:
+            B.moe4_expert_up_w4a8(shape, c["x8"], c["xs"], offsets, perm_src, a13, None, *h_tmp)
+        else:
+            B.moe4_expert_up(shape, c["x"], offsets, perm_src, a13, h_tmp)
 
     def down_routed(i):
         offsets, _ = plans[i % chunks]
-        B.moe4_expert_down(shape, hs[i % chunks], offsets, weights[(i // chunks) % copies][1], y)
+        a2 = weights[(i // chunks) % copies][1]
+        if fp8:
+            B.moe4_expert_down_w4a8(shape, *hs[i % chunks], offsets, a2, y)
+        else:
+            B.moe4_expert_down(shape, hs[i % chunks], offsets, a2, y)
 
     def up_shared(i):
-        B.moe4_expert_up(shape, per_chunk[i % chunks]["x"], None, None, s13, hd_tmp)
+        c = per_chunk[i % chunks]
+        if fp8:
+            B.moe4_expert_up_w4a8(shape, c["x8"], c["xs"], None, None, s13, None, *hd_tmp)
+        else:
+            B.moe4_expert_up(shape, c["x"], None, None, s13, hd_tmp)
 
     def down_shared(i):
-        B.moe4_expert_down(shape, hds[i % chunks], None, s2, yd)
+        if fp8:
+            B.moe4_expert_down_w4a8(shape, *hds[i % chunks], None, s2, yd)
+        else:
+            B.moe4_expert_down(shape, hds[i % chunks], None, s2, yd)
 
-    prefill_kind = T * w.k >= 40 * w.E
-    kind_name = "ffn_prefill_kernel" if prefill_kind else "ffn_decode_kernel"
+    # the FP8 form always runs the tiled GEMM; the BF16 form streams below 40 rows per expert
+    prefill_kind = fp8 or T * w.k >= 40 * w.E
+    kind_name = "ffn_prefill_fp8_kernel" if fp8 else ("ffn_prefill_kernel" if prefill_kind else "ffn_decode_kernel")
+    peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
     launches = [("up_routed", up_routed, True, False), ("down_routed", down_routed, False, False)]
     if s13 is not None:
         launches += [("up_shared", up_shared, True, True), ("down_shared", down_shared, False, True)]
@@ -479,7 +532,7 @@ def main():
         mean_s = ev0.elapsed_time(ev1) / (k2 * chunks) / 1e3
         nb = fl = 0
         for idx in routing:
-            b, f, _ = ffn_work(w, T, idx, up, dense)
+            b, f, _ = ffn_work(w, T, idx, up, dense, fp8)
             nb += b
             fl += f
         nb /= chunks
@@ -502,24 +555,26 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
     else:
         achieved = flops / up_mean_s / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
-    roofline["traffic"] = measured_traffic(args.config, KERNEL_SOURCES["prefill" if prefill_kind else "decode"])
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    roofline["traffic"] = measured_traffic(args.config + ("_w4a8" if fp8 else ""),
+                                           KERNEL_SOURCES["prefill" if prefill_kind else "decode"])
     roofline.update({"kernel": dom["kernel"] + " (routed expert up: W13 dequant-MFMA + SwiGLU)",
                      "mean_us": dom["mean_us"], "algorithmic_bytes": int(nbytes),
                      "algorithmic_flops": int(flops)})
     for v in kernels.values():
-        v["frac_of_peak"] = round(v["TFLOP_s"] / BF16_PEAK_TFLOPS if prefill_kind else
+        v["frac_of_peak"] = round(v["TFLOP_s"] / peak if prefill_kind else
                                   v["GB_s"] / HBM_PEAK_GBS, 4)
 
     cfg = {"workload": f"{args.config}: T={T}{'x%d chunks' % chunks if chunks > 1 else ''} H={w.H} "
                        f"E={w.E}{'+%d shared' % w.n_shared if w.n_shared else ''} top-{w.k} I={w.I}, "
-                       f"W4A16 (E2M1 + E4M3/16 + FP32)",
+                       + ("W4A8 (E2M1 + E4M3/16 + FP32 weights rounded to E4M3; E4M3 activations, "
+                          "E8M0 scale per 32)" if fp8 else "W4A16 (E2M1 + E4M3/16 + FP32)"),
            "T": T * chunks, "H": w.H, "E": w.E, "k": w.k, "I": w.I, "n_shared": w.n_shared,
            "weight_copies_rotated": copies, "routing": w.routing, "side_stream": use_side}
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8" if fp8 else "bf16",
            "data": "synthetic", "config": cfg, "roofline": roofline, "kernels": kernels}
     if cpu is not None:
         out["cpu_baseline"] = cpu

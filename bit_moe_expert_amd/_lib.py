@@ -6,7 +6,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, Structure, c_char_p, c_float, c_int, c_int32, c_size_t, c_void_p
+from ctypes import POINTER, Structure, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe4.so")
@@ -62,6 +62,16 @@ SIGNATURES = {
     "moe4_layer_side": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, _W4, _W4, _W4, _W4, c_void_p,
                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                 c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe4_quant_mxfp8": (c_int, [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe4_w4a8_workspace_bytes": (c_size_t, [_SHAPE]),
+    "moe4_expert_ffn_w4a8": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, _W4, _W4, c_void_p, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]),
+    "moe4_expert_up_w4a8": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, c_void_p, _W4, c_void_p, c_void_p,
+                                    c_void_p, c_void_p]),
+    "moe4_expert_down_w4a8": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, _W4, c_void_p, c_void_p]),
+    "moe4_layer_w4a8": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, _W4, _W4, _W4, _W4, c_void_p,
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                c_void_p]),
     "moe4_add_rmsnorm": (c_int, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_float, c_void_p,
                                  c_void_p, c_void_p]),
     "moe4_group_rmsnorm": (c_int, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_float, c_void_p,

@@ -222,6 +222,69 @@ def moe4_layer_noalloc(shape: Shape, x, w_router, logits, w13: DeviceW4, w2: Dev
         _ptr(normed_out, "normed_out", _BF16_LIKE, T * H), _stream(stream)))
 
 
+def moe4_quant_mxfp8(x, q, e, stream=None) -> None:
+    """Block-scaled FP8 of BF16 x [rows][K]: q uint8 [rows][K] E4M3 codes, e uint8
+    [rows][K/32] E8M0 scale bytes."""
+    rows, K = x.shape
+    check(_lib.load().moe4_quant_mxfp8(
+        rows, K, _ptr(x, "x", _BF16_LIKE), _ptr(q, "q", (torch.uint8,), rows * K),
+        _ptr(e, "e", (torch.uint8,), rows * (K // 32)), _stream(stream)))
+
+
+def moe4_w4a8_workspace_bytes(shape: Shape) -> int:
+    return int(_lib.load().moe4_w4a8_workspace_bytes(shape))
+
+
+def moe4_expert_ffn_w4a8(shape: Shape, x, offsets, perm_src, w13: DeviceW4, w2: DeviceW4, h, y, ws,
+                         stream=None) -> None:
+    rows = shape.T * shape.k if offsets is not None else shape.T
+    d13, d2 = w13.desc(), w2.desc()
+    check(_lib.load().moe4_expert_ffn_w4a8(
+        shape, _ptr(x, "x", _BF16_LIKE, shape.T * shape.H),
+        _ptr(offsets, "offsets", (torch.int32,)), _ptr(perm_src, "perm_src", (torch.int32,)),
+        d13, d2, _ptr(h, "h", _BF16_LIKE, rows * shape.I), _ptr(y, "y", _BF16_LIKE, rows * shape.H),
+        _ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe4_expert_up_w4a8(shape: Shape, x8, xs, offsets, perm_src, w13: DeviceW4, h, h8, hs,
+                        stream=None) -> None:
+    rows = shape.T * shape.k if offsets is not None else shape.T
+    T, H, I = shape.T, shape.H, shape.I
+    d13 = w13.desc()
+    check(_lib.load().moe4_expert_up_w4a8(
+        shape, _ptr(x8, "x8", (torch.uint8,), T * H), _ptr(xs, "xs", (torch.uint8,), T * H // 32),
+        _ptr(offsets, "offsets", (torch.int32,)), _ptr(perm_src, "perm_src", (torch.int32,)), d13,
+        _ptr(h, "h", _BF16_LIKE, rows * I), _ptr(h8, "h8", (torch.uint8,), rows * I),
+        _ptr(hs, "hs", (torch.uint8,), rows * I // 32), _stream(stream)))
+
+
+def moe4_expert_down_w4a8(shape: Shape, h8, hs, offsets, w2: DeviceW4, y, stream=None) -> None:
+    rows = shape.T * shape.k if offsets is not None else shape.T
+    d2 = w2.desc()
+    check(_lib.load().moe4_expert_down_w4a8(
+        shape, _ptr(h8, "h8", (torch.uint8,), rows * shape.I), _ptr(hs, "hs", (torch.uint8,), rows * shape.I // 32),
+        _ptr(offsets, "offsets", (torch.int32,)), d2, _ptr(y, "y", _BF16_LIKE, rows * shape.H), _stream(stream)))
+
+
+def moe4_layer_w4a8(shape: Shape, x, w_router, logits, w13: DeviceW4, w2: DeviceW4,
+                    shared13: Optional[DeviceW4], shared2: Optional[DeviceW4], residual, gamma,
+                    topk_idx, topk_w, residual_out, normed_out, ws, stream=None) -> None:
+    """The whole layer with the FP8 (W4A8) expert FFNs."""
+    T, H, E, k = shape.T, shape.H, shape.E, shape.k
+    d13, d2 = w13.desc(), w2.desc()
+    s13 = shared13.desc() if shared13 is not None else None
+    s2 = shared2.desc() if shared2 is not None else None
+    check(_lib.load().moe4_layer_w4a8(
+        shape, _ptr(x, "x", _BF16_LIKE, T * H), _ptr(w_router, "w_router", _BF16_LIKE, E * H),
+        _ptr(logits, "logits", (torch.float32,), T * E), d13, d2, s13, s2,
+        _ptr(residual, "residual", _BF16_LIKE, T * H), _ptr(gamma, "gamma", _BF16_LIKE, H),
+        _ptr(topk_idx, "topk_idx", (torch.int32,), T * k),
+        _ptr(topk_w, "topk_w", (torch.float32,), T * k),
+        _ptr(residual_out, "residual_out", _BF16_LIKE, T * H),
+        _ptr(normed_out, "normed_out", _BF16_LIKE, T * H),
+        _ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
 _SIDE_EVENTS = {}
 
 

@@ -128,6 +128,37 @@ moe4_status scratch_ptr(void** out) {
   return MOE4_OK;
 }
 
+// Workspace of the FP8 (W4A8) entry points: the plan, the block-scaled FP8 x and h
+// (codes and E8M0 scales), and y.
+struct W4a8Ws {
+  size_t offsets, perm_src, inv, perm_ws, x8, xs, h8, hs, y, total;
+};
+
+W4a8Ws w4a8_ws_layout(const moe4_shape* s) {
+  W4a8Ws l{};
+  const size_t pairs = (size_t)s->T * s->k;
+  const size_t rows = pairs + (size_t)s->T * s->n_shared;
+  size_t o = 0;
+  l.offsets = o;  o += align256((size_t)(s->E + 1) * 4);
+  l.perm_src = o; o += align256(pairs * 4);
+  l.inv = o;      o += align256(pairs * 4);
+  l.perm_ws = o;  o += align256(moe4::permute_workspace_bytes((long long)pairs, s->E));
+  l.x8 = o;       o += align256((size_t)s->T * s->H);
+  l.xs = o;       o += align256((size_t)s->T * (s->H / 32));
+  l.h8 = o;       o += align256(rows * s->I);
+  l.hs = o;       o += align256(rows * (s->I / 32));
+  l.y = o;        o += align256(rows * s->H * 2);
+  l.total = o;
+  return l;
+}
+
+moe4_status check_w4a8_shape(const moe4_shape* s) {
+  if (!moe4::prefill_shape_ok(s->H, s->I))
+    return fail(MOE4_ERR_UNSUPPORTED, "the FP8 (W4A8) form needs H %% 256 == 0 and I %% 128 == 0 (H=%d I=%d)",
+                s->H, s->I);
+  return MOE4_OK;
+}
+
 }  // namespace
 
 namespace moe4 {
@@ -498,6 +529,191 @@ moe4_status moe4_layer_noalloc(const moe4_shape* shape, const uint16_t* x, const
                                void* stream) {
   return layer_impl(shape, x, w_router, logits, w13, w2, shared13, shared2, residual, gamma, topk_idx, topk_w,
                     residual_out, normed_out, nullptr, 0, stream, nullptr, nullptr, nullptr, true);
+}
+
+moe4_status moe4_quant_mxfp8(int64_t rows, int32_t K, const uint16_t* x, uint8_t* q, uint8_t* e, void* stream) {
+  g_err[0] = 0;
+  if (rows < 0 || K <= 0) return fail(MOE4_ERR_INVALID_ARG, "negative or zero size (rows=%lld K=%d)", (long long)rows, K);
+  if (K % 32) return fail(MOE4_ERR_UNSUPPORTED, "K=%d is not a multiple of 32", K);
+  if (rows == 0) return MOE4_OK;
+  NEED(x, "x");
+  NEED(q, "q");
+  if (e == nullptr) return fail(MOE4_ERR_INVALID_ARG, "e is NULL");
+  hipError_t err = moe4::launch_mxfp8_quant(x, rows, K, q, e, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "mxfp8 quant launch");
+  return MOE4_OK;
+}
+
+size_t moe4_w4a8_workspace_bytes(const moe4_shape* shape) {
+  if (check_shape(shape) != MOE4_OK || check_w4a8_shape(shape) != MOE4_OK) return 0;
+  return w4a8_ws_layout(shape).total;
+}
+
+moe4_status moe4_expert_ffn_w4a8(const moe4_shape* shape, const uint16_t* x, const int32_t* offsets,
+                                 const int32_t* perm_src, const moe4_w4* w13, const moe4_w4* w2, uint16_t* h,
+                                 uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe4_status st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_w4a8_shape(shape))) return st;
+  if (shape->T == 0) return MOE4_OK;
+  if ((offsets == nullptr) != (perm_src == nullptr))
+    return fail(MOE4_ERR_INVALID_ARG, "offsets and perm_src must both be set or both be NULL");
+  NEED(x, "x");
+  if (offsets) {
+    NEED(offsets, "offsets");
+    NEED(perm_src, "perm_src");
+  }
+  if ((st = check_w4(w13, "w13"))) return st;
+  if ((st = check_w4(w2, "w2"))) return st;
+  if (h) NEED(h, "h");
+  NEED(y, "y");
+  const W4a8Ws L = w4a8_ws_layout(shape);
+  if (ws == nullptr || ws_bytes < L.total)
+    return fail(MOE4_ERR_WORKSPACE, "the FP8 FFN needs %zu workspace bytes, got %zu%s", L.total, ws_bytes,
+                ws ? "" : " (NULL)");
+  if (!aligned16(ws)) return fail(MOE4_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  char* b = static_cast<char*>(ws);
+  uint8_t* x8 = reinterpret_cast<uint8_t*>(b + L.x8);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(b + L.xs);
+  uint8_t* h8 = reinterpret_cast<uint8_t*>(b + L.h8);
+  uint8_t* hs = reinterpret_cast<uint8_t*>(b + L.hs);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = shape->T, H = shape->H, I = shape->I, k = shape->k;
+  const int G = offsets ? shape->E : 1;
+  hipError_t e = moe4::launch_mxfp8_quant(x, T, H, x8, xs, s);
+  if (e != hipSuccess) return hip_fail(e, "mxfp8 quant launch");
+  e = moe4::launch_ffn_up_prefill_fp8(x8, xs, offsets, perm_src, k, T, G, H, I, view(w13), h, h8, hs, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 ffn up launch");
+  e = moe4::launch_ffn_down_prefill_fp8(h8, hs, offsets, k, T, G, H, I, view(w2), y, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 ffn down launch");
+  return MOE4_OK;
+}
+
+moe4_status moe4_expert_up_w4a8(const moe4_shape* shape, const uint8_t* x8, const uint8_t* xs,
+                                const int32_t* offsets, const int32_t* perm_src, const moe4_w4* w13, uint16_t* h,
+                                uint8_t* h8, uint8_t* hs, void* stream) {
+  g_err[0] = 0;
+  moe4_status st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_w4a8_shape(shape))) return st;
+  if (shape->T == 0) return MOE4_OK;
+  if ((offsets == nullptr) != (perm_src == nullptr))
+    return fail(MOE4_ERR_INVALID_ARG, "offsets and perm_src must both be set or both be NULL");
+  NEED(x8, "x8");
+  if (xs == nullptr) return fail(MOE4_ERR_INVALID_ARG, "xs is NULL");
+  if (offsets) {
+    NEED(offsets, "offsets");
+    NEED(perm_src, "perm_src");
+  }
+  if ((st = check_w4(w13, "w13"))) return st;
+  if (h) NEED(h, "h");
+  NEED(h8, "h8");
+  if (hs == nullptr) return fail(MOE4_ERR_INVALID_ARG, "hs is NULL");
+  const int G = offsets ? shape->E : 1;
+  hipError_t e = moe4::launch_ffn_up_prefill_fp8(x8, xs, offsets, perm_src, shape->k, shape->T, G, shape->H,
+                                                 shape->I, view(w13), h, h8, hs, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 ffn up launch");
+  return MOE4_OK;
+}
+
+moe4_status moe4_expert_down_w4a8(const moe4_shape* shape, const uint8_t* h8, const uint8_t* hs,
+                                  const int32_t* offsets, const moe4_w4* w2, uint16_t* y, void* stream) {
+  g_err[0] = 0;
+  moe4_status st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_w4a8_shape(shape))) return st;
+  if (shape->T == 0) return MOE4_OK;
+  NEED(h8, "h8");
+  if (hs == nullptr) return fail(MOE4_ERR_INVALID_ARG, "hs is NULL");
+  if (offsets) NEED(offsets, "offsets");
+  if ((st = check_w4(w2, "w2"))) return st;
+  NEED(y, "y");
+  const int G = offsets ? shape->E : 1;
+  hipError_t e = moe4::launch_ffn_down_prefill_fp8(h8, hs, offsets, shape->k, shape->T, G, shape->H, shape->I,
+                                                   view(w2), y, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 ffn down launch");
+  return MOE4_OK;
+}
+
+moe4_status moe4_layer_w4a8(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router, float* logits,
+                            const moe4_w4* w13, const moe4_w4* w2, const moe4_w4* shared13,
+                            const moe4_w4* shared2, const uint16_t* residual, const uint16_t* gamma,
+                            int32_t* topk_idx, float* topk_w, uint16_t* residual_out, uint16_t* normed_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe4_status st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_w4a8_shape(shape))) return st;
+  if (shape->T == 0) return MOE4_OK;
+  NEED(x, "x");
+  if (w_router) NEED(w_router, "w_router");
+  NEED(logits, "logits");
+  if ((st = check_w4(w13, "w13"))) return st;
+  if ((st = check_w4(w2, "w2"))) return st;
+  if (shape->n_shared) {
+    if ((st = check_w4(shared13, "shared13"))) return st;
+    if ((st = check_w4(shared2, "shared2"))) return st;
+  }
+  NEED(residual, "residual");
+  NEED(gamma, "gamma");
+  NEED(topk_idx, "topk_idx");
+  NEED(topk_w, "topk_w");
+  NEED(residual_out, "residual_out");
+  NEED(normed_out, "normed_out");
+  const W4a8Ws L = w4a8_ws_layout(shape);
+  if (ws == nullptr || ws_bytes < L.total)
+    return fail(MOE4_ERR_WORKSPACE, "the FP8 layer needs %zu workspace bytes, got %zu%s", L.total, ws_bytes,
+                ws ? "" : " (NULL)");
+  if (!aligned16(ws)) return fail(MOE4_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  char* b = static_cast<char*>(ws);
+  int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  int32_t* perm_src = reinterpret_cast<int32_t*>(b + L.perm_src);
+  int32_t* inv = reinterpret_cast<int32_t*>(b + L.inv);
+  uint8_t* x8 = reinterpret_cast<uint8_t*>(b + L.x8);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(b + L.xs);
+  uint8_t* h8 = reinterpret_cast<uint8_t*>(b + L.h8);
+  uint8_t* hs = reinterpret_cast<uint8_t*>(b + L.hs);
+  uint16_t* y = reinterpret_cast<uint16_t*>(b + L.y);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = shape->T, H = shape->H, E = shape->E, k = shape->k, I = shape->I;
+  const size_t pairs = (size_t)T * k;
+  hipError_t e;
+  if (w_router) {
+    e = moe4::launch_router_logits(x, w_router, logits, T, H, E, s);
+    if (e != hipSuccess) return hip_fail(e, "router_logits launch");
+  }
+  if (moe4::route_plan_fits(T, k)) {
+    e = moe4::launch_route_plan(logits, T, E, k, topk_idx, topk_w, offsets, perm_src, inv, s);
+    if (e != hipSuccess) return hip_fail(e, "route_plan launch");
+  } else {
+    e = moe4::launch_topk_softmax(logits, topk_idx, topk_w, T, E, k, s);
+    if (e != hipSuccess) return hip_fail(e, "topk_softmax launch");
+    e = moe4::launch_permute(topk_idx, (long long)pairs, E, offsets, perm_src, inv, b + L.perm_ws, s);
+    if (e != hipSuccess) return hip_fail(e, "permute launch");
+  }
+  e = moe4::launch_mxfp8_quant(x, T, H, x8, xs, s);
+  if (e != hipSuccess) return hip_fail(e, "mxfp8 quant launch");
+  e = moe4::launch_ffn_up_prefill_fp8(x8, xs, offsets, perm_src, k, T, E, H, I, view(w13), nullptr, h8, hs, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 ffn up launch");
+  e = moe4::launch_ffn_down_prefill_fp8(h8, hs, offsets, k, T, E, H, I, view(w2), y, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 ffn down launch");
+  const uint16_t* shared_y = nullptr;
+  if (shape->n_shared) {
+    uint8_t* h8s = h8 + pairs * I;
+    uint8_t* hss = hs + pairs * (I / 32);
+    uint16_t* ys = y + pairs * H;
+    e = moe4::launch_ffn_up_prefill_fp8(x8, xs, nullptr, nullptr, k, T, 1, H, I, view(shared13), nullptr, h8s,
+                                        hss, s);
+    if (e != hipSuccess) return hip_fail(e, "shared fp8 ffn up launch");
+    e = moe4::launch_ffn_down_prefill_fp8(h8s, hss, nullptr, k, T, 1, H, I, view(shared2), ys, s);
+    if (e != hipSuccess) return hip_fail(e, "shared fp8 ffn down launch");
+    shared_y = ys;
+  }
+  e = moe4::launch_combine_norm(y, inv, topk_w, shared_y, residual, gamma, residual_out, normed_out, T, H, k,
+                                shape->eps, s);
+  if (e != hipSuccess) return hip_fail(e, "combine_norm launch");
+  return MOE4_OK;
 }
 
 moe4_status moe4_layer_side(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,

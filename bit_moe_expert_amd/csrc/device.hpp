@@ -118,6 +118,44 @@ __device__ __forceinline__ uint32_t load_b16(BufRes r, int off) {
 }
 
 // ---------------------------------------------------------------------------
+// Block-scaled FP8 activations (the W4A8 prefill variant): 32 consecutive BF16
+// values (4 dwords of pairs, element order low half first) -> 32 OCP E4M3 bytes and
+// the block's power-of-two exponent e (stored by callers as the E8M0 byte e + 127).
+// e is the smallest integer for which the block's largest magnitude times 2^-e is at
+// most 448 (so nothing saturates), 0 for an all-zero block, clamped to [-127, 127];
+// each value times 2^-e (exact) is rounded to E4M3, nearest with ties to even
+// (v_cvt_pk_fp8_f32; checked bit for bit against that rule on gfx950, including the
+// subnormal range).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int mxfp8_block(const u32x4 v[4], u32x4 out[2]) {
+  uint32_t amax = 0;  // BF16 magnitudes order as their bit patterns
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = max(amax, max(v[i][j] & 0x7fffu, (v[i][j] >> 16) & 0x7fffu));
+  int e = 0;
+  if (amax != 0) {
+    const float a = __uint_as_float(amax << 16);
+    const int E = __builtin_amdgcn_frexp_expf(a) - 1;        // a = m * 2^E, 1 <= m < 2
+    const float m = __builtin_amdgcn_frexp_mantf(a) * 2.0f;  // exact
+    e = E - 8 + (m > 1.75f ? 1 : 0);
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      const float f0 = __builtin_ldexpf(bf16_lo(v[i][j]), -e), f1 = __builtin_ldexpf(bf16_hi(v[i][j]), -e);
+      const float f2 = __builtin_ldexpf(bf16_lo(v[i][j + 1]), -e), f3 = __builtin_ldexpf(bf16_hi(v[i][j + 1]), -e);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, w, true);
+      out[i / 2][(i % 2) * 2 + j / 2] = (uint32_t)w;
+    }
+  }
+  return e;
+}
+
+// ---------------------------------------------------------------------------
 // Misc
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }

@@ -56,6 +56,17 @@ hipError_t launch_ffn_up_prefill(const uint16_t* x, const int32_t* offsets, cons
 hipError_t launch_ffn_down_prefill(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H,
                                    int I, W4View w2, uint16_t* y, hipStream_t s);
 
+// FP8 (W4A8) prefill form: activations as block-scaled E4M3 (32 values per E8M0
+// scale), weights rounded to E4M3, block-scaled FP8 MFMAs. x [rows][K] BF16 ->
+// q [rows][K] E4M3 + e [rows][K/32] E8M0 (K % 32 == 0).
+hipError_t launch_mxfp8_quant(const uint16_t* x, long long rows, int K, uint8_t* q, uint8_t* e, hipStream_t s);
+// up: h8/hs (the down projection's FP8 input) always, BF16 h too when h != NULL
+hipError_t launch_ffn_up_prefill_fp8(const uint8_t* x8, const uint8_t* xs, const int32_t* offsets,
+                                     const int32_t* perm_src, int k, int T, int G, int H, int I, W4View w13,
+                                     uint16_t* h, uint8_t* h8, uint8_t* hs, hipStream_t s);
+hipError_t launch_ffn_down_prefill_fp8(const uint8_t* h8, const uint8_t* hs, const int32_t* offsets, int k, int T,
+                                       int G, int H, int I, W4View w2, uint16_t* y, hipStream_t s);
+
 // o = residual + sum_j w_j * y[inv[t*k+j]] (+ shared); n = rmsnorm(o) * gamma.
 hipError_t launch_combine_norm(const uint16_t* y, const int32_t* inv, const float* w,
                                const uint16_t* shared_y, const uint16_t* residual,

@@ -257,6 +257,70 @@ moe4_status moe4_layer_side(const moe4_shape* shape, const uint16_t* x, const ui
                             size_t ws_bytes, void* stream, void* side_stream, void* fork_event,
                             void* join_event);
 
+/* The FP8 (W4A8) prefill variant: the expert FFN with FP8 E4M3 matmul inputs, for
+ * prompt processing (the Qiita TensorFold 1.1.x article, section "Why it still does not
+ * reach 0.6.6", names an FP8 prompt-matmul option; the PR804 article's NVFP4 section
+ * tells W4A16 apart from lower-precision activations). The pages fix neither the
+ * activation format nor the weight rounding; this library reads them as follows, and
+ * every result is defined by this reading:
+ *   - activations (x into the up projection, the BF16 h into the down projection) are
+ *     quantised in blocks of 32 consecutive values along K: each block gets a power-of-
+ *     two scale 2^e, e the smallest integer for which the block's largest magnitude
+ *     times 2^-e is at most 448 (the largest E4M3 value, so nothing saturates; e = 0
+ *     for an all-zero block; e clamped to [-127, 127]), and each value times 2^-e is
+ *     rounded to E4M3, nearest with ties to even;
+ *   - each weight, code * E4M3 block scale (exact), is rounded to E4M3 the same way,
+ *     saturating at +-448; the FP32 tensor scale multiplies the FP32 sums;
+ *   - h and y are BF16 as in the W4A16 path.
+ * Shapes: H a multiple of 256, I a multiple of 128 (else MOE4_ERR_UNSUPPORTED). Inputs
+ * must be finite.
+ *
+ * moe4_quant_mxfp8: the activation quantiser alone.
+ *   x         BF16 [rows][K] in; K a multiple of 32.
+ *   q         uint8 [rows][K] out: the E4M3 codes (OCP E4M3FN bytes).
+ *   e         uint8 [rows][K/32] out: each block's scale as an E8M0 byte, e + 127.
+ *   rows == 0 does nothing; x and q 16-byte aligned. */
+moe4_status moe4_quant_mxfp8(int64_t rows, int32_t K, const uint16_t* x, uint8_t* q, uint8_t* e,
+                             void* stream);
+
+/* Device workspace moe4_expert_ffn_w4a8 and moe4_layer_w4a8 need (0 for an invalid or
+ * unsupported shape). */
+size_t moe4_w4a8_workspace_bytes(const moe4_shape* shape);
+
+/* moe4_expert_ffn with the FP8 matmul inputs above. Arguments as for moe4_expert_ffn,
+ * plus:
+ *   h         BF16 [R][I] out, or NULL (h is then kept only in its FP8 form, in ws).
+ *   ws        device workspace of at least moe4_w4a8_workspace_bytes(shape), 16-byte
+ *             aligned: it holds x and h in their block-scaled FP8 form. */
+moe4_status moe4_expert_ffn_w4a8(const moe4_shape* shape, const uint16_t* x, const int32_t* offsets,
+                                 const int32_t* perm_src, const moe4_w4* w13, const moe4_w4* w2,
+                                 uint16_t* h, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/* The two halves of moe4_expert_ffn_w4a8 on activations already in their FP8 form
+ * (for callers that schedule them apart, and for timing the dominant one alone).
+ * Arguments as for moe4_expert_ffn_w4a8, plus:
+ *   x8, xs    moe4_quant_mxfp8 of x: uint8 [T][H] E4M3 codes (16-byte aligned) and
+ *             uint8 [T][H/32] E8M0 scale bytes.
+ *   h8, hs    out of moe4_expert_up_w4a8 and in of moe4_expert_down_w4a8: h in the
+ *             same form, uint8 [R][I] (16-byte aligned) and uint8 [R][I/32] (R = T*k,
+ *             dense mode T), the BF16 h quantised exactly as moe4_quant_mxfp8 does.
+ *   h         BF16 [R][I] out of the up half, or NULL. */
+moe4_status moe4_expert_up_w4a8(const moe4_shape* shape, const uint8_t* x8, const uint8_t* xs,
+                                const int32_t* offsets, const int32_t* perm_src, const moe4_w4* w13,
+                                uint16_t* h, uint8_t* h8, uint8_t* hs, void* stream);
+moe4_status moe4_expert_down_w4a8(const moe4_shape* shape, const uint8_t* h8, const uint8_t* hs,
+                                  const int32_t* offsets, const moe4_w4* w2, uint16_t* y, void* stream);
+
+/* moe4_layer with the routed and the shared expert FFN in the FP8 form above (routing,
+ * plan, combine and norm unchanged). Arguments as for moe4_layer; ws is at least
+ * moe4_w4a8_workspace_bytes(shape). */
+moe4_status moe4_layer_w4a8(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                            float* logits, const moe4_w4* w13, const moe4_w4* w2,
+                            const moe4_w4* shared13, const moe4_w4* shared2,
+                            const uint16_t* residual, const uint16_t* gamma, int32_t* topk_idx,
+                            float* topk_w, uint16_t* residual_out, uint16_t* normed_out, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* Neighbouring glue: the two RMSNorm launches of a decode step beside the MoE layer
  * (#627: add_rmsnorm in the Oct 10 list of the other glue ops, add_rmsnorm and
  * group_rmsnorm in the Oct 14 per-step breakdown). Neither takes a moe4_shape.

@@ -231,3 +231,48 @@ def test_noalloc_layer_checks():
     # the header's scratch size is the one the binding knows
     m = re.search(r"#define MOE4_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
     assert int(m.group(1)) << int(m.group(2)) == _lib.MOE4_NOALLOC_SCRATCH_BYTES
+
+
+def test_w4a8_checks():
+    """The FP8 (W4A8) entry points: shape limits, workspace size, pointer and descriptor
+    checks, all before any GPU call."""
+    lib = _lib.load()
+    E_ARG, E_UNS, E_WS, OK = (_lib.MOE4_ERR_INVALID_ARG, _lib.MOE4_ERR_UNSUPPORTED,
+                              _lib.MOE4_ERR_WORKSPACE, _lib.MOE4_OK)
+    w = W4(FAKE, FAKE, FAKE, _lib.MOE4_W4_TILED)
+    # the quantiser
+    assert lib.moe4_quant_mxfp8(4, 48, FAKE, FAKE, FAKE, None) == E_UNS
+    assert lib.moe4_quant_mxfp8(-1, 64, FAKE, FAKE, FAKE, None) == E_ARG
+    assert lib.moe4_quant_mxfp8(4, 0, FAKE, FAKE, FAKE, None) == E_ARG
+    assert lib.moe4_quant_mxfp8(4, 64, FAKE, None, FAKE, None) == E_ARG
+    assert lib.moe4_quant_mxfp8(4, 64, FAKE + 8, FAKE, FAKE, None) == E_ARG
+    assert lib.moe4_quant_mxfp8(0, 64, None, None, None, None) == OK
+    # workspace: x8 + scales, h8 + scales and y over the routed and shared rows
+    s = shape(n_shared=1)
+    need = lib.moe4_w4a8_workspace_bytes(s)
+    rows = 8 * 8 + 8
+    assert need >= 8 * 2048 * (1 + 1 / 32) + rows * (768 * (1 + 1 / 32) + 2048 * 2)
+    assert lib.moe4_w4a8_workspace_bytes(shape(H=2048 + 128)) == 0   # H % 256
+    assert lib.moe4_w4a8_workspace_bytes(shape(I=768 + 64)) == 0     # I % 128
+    assert lib.moe4_w4a8_workspace_bytes(None) == 0
+    # FFN
+    assert lib.moe4_expert_ffn_w4a8(shape(I=832), FAKE, FAKE, FAKE, w, w, None, FAKE, FAKE, 1 << 40,
+                                    None) == E_UNS
+    st = lib.moe4_expert_ffn_w4a8(shape(), FAKE, FAKE, FAKE, w, w, None, FAKE, FAKE, 16, None)
+    assert st == E_WS
+    st = lib.moe4_expert_ffn_w4a8(shape(), FAKE, FAKE, None, w, w, None, FAKE, FAKE, 1 << 40, None)
+    assert st == E_ARG
+    bad = W4(FAKE, FAKE, FAKE, 0)
+    st = lib.moe4_expert_ffn_w4a8(shape(), FAKE, FAKE, FAKE, w, bad, None, FAKE, FAKE, 1 << 40, None)
+    assert st == E_ARG and b"w2.layout" in lib.moe4_last_error()
+    st = lib.moe4_expert_ffn_w4a8(shape(), FAKE, FAKE, FAKE, w, w, None, FAKE, FAKE + 8, 1 << 40, None)
+    assert st == E_ARG and b"ws" in lib.moe4_last_error()
+    # layer
+    st = lib.moe4_layer_w4a8(s, FAKE, None, FAKE, w, w, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, 1 << 40, None)
+    assert st == E_ARG and b"shared13" in lib.moe4_last_error()
+    st = lib.moe4_layer_w4a8(s, FAKE, None, FAKE, w, w, w, w, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, need - 1, None)
+    assert st == E_WS
+    assert lib.moe4_layer_w4a8(shape(T=0), None, None, None, None, None, None, None, None, None, None, None,
+                               None, None, None, 0, None) == OK

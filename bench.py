@@ -76,23 +76,31 @@ def parse():
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {"decode": os.path.join(ROOT, "bit_moe_expert_amd", "csrc", "ffn_decode.hip"),
-                  "prefill": os.path.join(ROOT, "bit_moe_expert_amd", "csrc", "ffn_prefill.hip")}
+_CSRC = os.path.join(ROOT, "bit_moe_expert_amd", "csrc")
+# the source files each dominant kernel is built from
+KERNEL_SOURCES = {
+    "decode": [os.path.join(_CSRC, f) for f in ("ffn_decode.hip", "device.hpp")],
+    "prefill": [os.path.join(_CSRC, f) for f in ("ffn_prefill.hip", "prefill_common.hpp", "device.hpp")],
+    "prefill_fp8": [os.path.join(_CSRC, f) for f in ("ffn_prefill_fp8.hip", "prefill_common.hpp", "device.hpp")],
+}
 
 
-def source_sha(path):
+def source_sha(paths):
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(config, kernel_source):
+def measured_traffic(config, kernel_sources):
     """HBM bytes per launch of the dominant kernel from a committed counter summary
     (``profiles/*_traffic.md``, its ``machine:`` line), if one was taken on this
     workload with the current kernel source; else None."""
     if not os.path.isdir(PROFILES):
         return None
-    want = source_sha(kernel_source)
+    want = source_sha(kernel_sources)
     for name in sorted(os.listdir(PROFILES)):
         if not name.endswith("_traffic.md"):
             continue
@@ -558,7 +566,8 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
     roofline["traffic"] = measured_traffic(args.config + ("_w4a8" if fp8 else ""),
-                                           KERNEL_SOURCES["prefill" if prefill_kind else "decode"])
+                                           KERNEL_SOURCES["prefill_fp8" if fp8 else
+                                                          "prefill" if prefill_kind else "decode"])
     roofline.update({"kernel": dom["kernel"] + " (routed expert up: W13 dequant-MFMA + SwiGLU)",
                      "mean_us": dom["mean_us"], "algorithmic_bytes": int(nbytes),
                      "algorithmic_flops": int(flops)})

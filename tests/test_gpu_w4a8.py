@@ -394,3 +394,58 @@ def test_w4a8_halves_compose_and_h_quantisation():
     B.moe4_expert_up_w4a8(shape, x8, xs, offs, perms, w13, None, h8b, hsb)
     torch.cuda.synchronize()
     assert torch.equal(h8b, h8) and torch.equal(hsb, hs)
+
+
+def test_layer_w4a8_canonical_weights_same_bits():
+    """Weights in the canonical (checkpoint) layout run the same kernels and give the
+    same bits as the tiled layout, and the layer meets the W4A8 bar."""
+    w = wl.Workload("w4a8_canon", T=96, H=512, E=8, k=2, I=256, routing="zipf", n_shared=1)
+    inp = wl.make_inputs(w, seed=21)
+    tiled = GpuLayerW4A8(inp, weights=upload_weights(inp, "tiled")).run()
+    canon = GpuLayerW4A8(inp, weights=upload_weights(inp, "canonical")).run()
+    for a, b in zip(tiled, canon):
+        assert np.array_equal(a, b)
+    ref = oracle.layer_w4a8(inp)
+    assert np.array_equal(tiled[0], ref["idx"])
+    assert_layer_close_w4a8(tiled[2], tiled[3], ref, inp, "w4a8 canonical")
+
+
+def test_w4a8_t0_is_a_noop():
+    """T = 0 enqueues nothing and leaves the outputs untouched."""
+    w = wl.workload("tiny")
+    shape = B.make_shape(0, w.H, w.E, w.k, w.I)
+    inp = wl.make_inputs(w, seed=0, T=1)
+    w13, w2 = upload_weights(inp)[:2]
+    y = torch.full((4, w.H), 7, dtype=torch.int16, device="cuda")
+    x = to_dev(inp.x)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    B.moe4_expert_ffn_w4a8(shape, x, None, None, w13, w2, None, y, ws)
+    q = torch.full((1, w.H), 3, dtype=torch.uint8, device="cuda")
+    e = torch.full((1, w.H // 32), 3, dtype=torch.uint8, device="cuda")
+    B.moe4_quant_mxfp8(x[:0], q, e)
+    torch.cuda.synchronize()
+    assert bool((y == 7).all()) and bool((q == 3).all()) and bool((e == 3).all())
+
+
+def test_expert_ffn_w4a8_all_rows_one_expert():
+    """Every routed row on one expert of many (k = 1): a run of full tiles, a ragged
+    last tile, and 63 empty experts in the schedule."""
+    w = wl.Workload("w4a8_one", T=700, H=512, E=64, k=1, I=256, routing="normal")
+    inp = wl.make_inputs(w, seed=22)
+    idx = np.full((w.T, 1), 37, dtype=np.int32)
+    off, perm, inv = oracle.permute(idx, w.E)
+    note("w4a8 expert ffn: 700 rows on expert 37 of 64")
+    _check_routed(inp, w, off, perm)
+
+
+@pytest.mark.parametrize("name", ["decode_t1", "decode_t8"])
+def test_layer_w4a8_decode_shapes_with_shared(name):
+    """The FP8 form at decode shapes (one or eight tokens) with a shared expert: the
+    prefill GEMM on a few rows per expert, dense mode with T < one tile."""
+    w = dataclasses.replace(wl.workload(name), n_shared=1)
+    inp = wl.make_inputs(w, seed=23)
+    condition_router_margin(inp)
+    idx, tw, o, n = GpuLayerW4A8(inp).run()
+    ref = oracle.layer_w4a8(inp)
+    assert np.array_equal(idx, ref["idx"])
+    assert_layer_close_w4a8(o, n, ref, inp, f"w4a8 {name} + shared")

@@ -22,7 +22,11 @@ Timed passes:
      weights + scales, activations in, h out) or flops divided by the mean launch
      duration give ``roofline.achieved``;
   3. the other expert-FFN launches of a layer call (routed down; shared up and down),
-     timed the same way, reported under ``kernels``.
+     timed the same way, reported under ``kernels`` with their sum (``ffn_total``);
+  4. the other steps through their own entry points (route, permute, combine_norm),
+     each call captured into a HIP graph and the graph replayed between the events (an
+     eager loop of these short launches would time the host), reported under
+     ``kernels`` with their algorithmic bytes.
 The fp64 oracle is timed on the host (``cpu_baseline``) on a bounded sample of the
 same tokens, one worker process per host core, before the GPU is touched.
 Prints one JSON line.
@@ -215,6 +219,9 @@ def glue_main(args):
     the stream. Input copies are rotated so that at least 1 GiB is touched, up to 16
     copies: decode-sized rows then stay cache-resident, as they are after the previous
     kernel wrote them, instead of each launch paying for fresh pages."""
+    # launches timed (0 = 2048: a short launch, a few ms in all) and untimed first
+    args.steps = args.steps or 2048
+    args.warmup = args.warmup if args.warmup >= 0 else 20
     import numpy as np
     import torch
 
@@ -290,7 +297,7 @@ def glue_main(args):
     desc = f"group={G}" if not add else "o = x + residual"
     out = {"metric": f"{args.op} rows/s", "value": round(T / mean_s, 1), "unit": "rows/s", "n_gpus": 1,
            "steps": replays * per_graph, "warmup": args.warmup, "ms_per_step": round(mean_s * 1e3, 6),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8" if fp8 else "bf16",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic",
            "config": {"workload": f"{args.op} over {T} rows of H={H} BF16 ({desc}), rows of the "
                                   f"{args.config} workload; launches replayed from a HIP graph",
@@ -554,6 +561,73 @@ def main():
             f"launches; {nb / 1e6:.1f} MB, {fl / 1e9:.2f} GFLOP per launch -> {nb / mean_s / 1e9:.0f} GB/s, "
             f"{fl / mean_s / 1e12:.1f} TFLOP/s")
 
+    # the expert FFN as a whole: every FFN launch of a layer call (both GEMMs, routed and
+    # shared), total work over total time
+    tot_us = sum(v["mean_us"] for v in kernels.values())
+    tot_b = sum(v["algorithmic_bytes"] for v in kernels.values())
+    tot_f = sum(v["algorithmic_flops"] for v in kernels.values())
+    kernels["ffn_total"] = {"kernel": "every expert-FFN launch of a layer call", "mean_us": round(tot_us, 3),
+                            "algorithmic_bytes": int(tot_b), "algorithmic_flops": int(tot_f),
+                            "GB_s": round(tot_b / tot_us / 1e3, 1), "TFLOP_s": round(tot_f / tot_us / 1e6, 1)}
+
+    # the other steps through their own entry points, timed the same way (route: the router
+    # GEMV when the logits are computed, then top-k; permute; combine + RMSNorm)
+    res_o = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
+    res_n = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
+    invs = []
+    for c, (offsets, perm_src) in zip(per_chunk, plans):
+        inv = torch.empty(pairs, dtype=torch.int32, device="cuda")
+        B.moe4_route(shape, c["x"] if wr is not None else None, wr, c["logits"], topk_idx, topk_w)
+        B.moe4_permute(shape, topk_idx, offsets, perm_src, inv, pws)
+        invs.append(inv)
+    torch.cuda.synchronize()
+    p_off = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
+    p_src = torch.empty(pairs, dtype=torch.int32, device="cuda")
+    p_inv = torch.empty(pairs, dtype=torch.int32, device="cuda")
+    glue = {
+        "route": (lambda i: B.moe4_route(shape, per_chunk[i % chunks]["x"] if wr is not None else None, wr,
+                                         per_chunk[i % chunks]["logits"], topk_idx, topk_w),
+                  (T * w.H * 2 + w.E * w.H * 2 + T * w.E * 4 if wr is not None else T * w.E * 4) + T * w.k * 8),
+        "permute": (lambda i: B.moe4_permute(shape, topk_idx, p_off, p_src, p_inv, pws),
+                    T * w.k * 4 + (w.E + 1) * 4 + 2 * T * w.k * 4),
+        "combine_norm": (lambda i: B.moe4_combine_norm(shape, y, invs[i % chunks], topk_w,
+                                                       yd if s13 is not None else None,
+                                                       per_chunk[i % chunks]["residual"], gamma, res_o, res_n),
+                         pairs * w.H * 2 + (T * w.H * 2 if s13 is not None else 0) + T * w.H * 2 + w.H * 2
+                         + pairs * 8 + 2 * T * w.H * 2),
+    }
+    # These launches are short: an eager loop would time the host's launch rate, so each
+    # entry point's calls are captured into a HIP graph and replayed between the events.
+    per_graph = 32 * chunks
+    for name, (fn, nb) in glue.items():
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(3 * chunks):
+                fn(i)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(per_graph):
+                fn(i)
+        torch.cuda.synchronize()
+        replays = max(2, k2 * chunks // per_graph)
+        graph.replay()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        mean_s = ev0.elapsed_time(ev1) / (replays * per_graph) / 1e3
+        del graph
+        kernels[name] = {"kernel": f"moe4_{name} (entry point, HIP graph replay)",
+                         "mean_us": round(mean_s * 1e6, 3), "launches": replays * per_graph,
+                         "algorithmic_bytes": int(nb), "GB_s": round(nb / mean_s / 1e9, 1)}
+        log(f"pass 4: {name} mean {mean_s * 1e6:.2f} us over {replays * per_graph} calls (graph replay); "
+            f"{nb / 1e6:.2f} MB -> {nb / mean_s / 1e9:.0f} GB/s")
+
     dom = kernels["up_routed"]
     up_mean_s = dom["mean_us"] / 1e6
     nbytes, flops = dom["algorithmic_bytes"], dom["algorithmic_flops"]
@@ -572,8 +646,10 @@ def main():
                      "mean_us": dom["mean_us"], "algorithmic_bytes": int(nbytes),
                      "algorithmic_flops": int(flops)})
     for v in kernels.values():
-        v["frac_of_peak"] = round(v["TFLOP_s"] / peak if prefill_kind else
-                                  v["GB_s"] / HBM_PEAK_GBS, 4)
+        if "TFLOP_s" in v:  # the FFN launches: against the roofline of their kind
+            v["frac_of_peak"] = round(v["TFLOP_s"] / peak if prefill_kind else v["GB_s"] / HBM_PEAK_GBS, 4)
+        else:               # the glue: against HBM
+            v["frac_of_peak"] = round(v["GB_s"] / HBM_PEAK_GBS, 4)
 
     cfg = {"workload": f"{args.config}: T={T}{'x%d chunks' % chunks if chunks > 1 else ''} H={w.H} "
                        f"E={w.E}{'+%d shared' % w.n_shared if w.n_shared else ''} top-{w.k} I={w.I}, "

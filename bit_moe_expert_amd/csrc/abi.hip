@@ -536,6 +536,8 @@ moe4_status moe4_quant_mxfp8(int64_t rows, int32_t K, const uint16_t* x, uint8_t
   if (rows < 0 || K <= 0) return fail(MOE4_ERR_INVALID_ARG, "negative or zero size (rows=%lld K=%d)", (long long)rows, K);
   if (K % 32) return fail(MOE4_ERR_UNSUPPORTED, "K=%d is not a multiple of 32", K);
   if (rows == 0) return MOE4_OK;
+  if (rows > (1LL << 31) / (K / 32) * 256)  // one thread per block of 32: the grid stays below 2^31
+    return fail(MOE4_ERR_UNSUPPORTED, "rows=%lld x K=%d is too large for one launch", (long long)rows, K);
   NEED(x, "x");
   NEED(q, "q");
   if (e == nullptr) return fail(MOE4_ERR_INVALID_ARG, "e is NULL");

@@ -279,7 +279,8 @@ moe4_status moe4_layer_side(const moe4_shape* shape, const uint16_t* x, const ui
  *   x         BF16 [rows][K] in; K a multiple of 32.
  *   q         uint8 [rows][K] out: the E4M3 codes (OCP E4M3FN bytes).
  *   e         uint8 [rows][K/32] out: each block's scale as an E8M0 byte, e + 127.
- *   rows == 0 does nothing; x and q 16-byte aligned. */
+ *   rows == 0 does nothing; x and q 16-byte aligned; rows * K / 32 below 2^39 (one launch),
+ *   else MOE4_ERR_UNSUPPORTED. */
 moe4_status moe4_quant_mxfp8(int64_t rows, int32_t K, const uint16_t* x, uint8_t* q, uint8_t* e,
                              void* stream);
 

@@ -247,6 +247,7 @@ def test_w4a8_checks():
     assert lib.moe4_quant_mxfp8(4, 64, FAKE, None, FAKE, None) == E_ARG
     assert lib.moe4_quant_mxfp8(4, 64, FAKE + 8, FAKE, FAKE, None) == E_ARG
     assert lib.moe4_quant_mxfp8(0, 64, None, None, None, None) == OK
+    assert lib.moe4_quant_mxfp8(1 << 40, 64, FAKE, FAKE, FAKE, None) == E_UNS
     # workspace: x8 + scales, h8 + scales and y over the routed and shared rows
     s = shape(n_shared=1)
     need = lib.moe4_w4a8_workspace_bytes(s)

@@ -56,8 +56,10 @@ Readings where the pages are silent (each is stated again where it is used):
 
 Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
 (closed forms, library routines, brute force on tiny inputs, invariants); ``layer``
-with a shared expert is pinned against an independent torch composition, and
-``tests/test_oracle_mutations.py`` checks that planted mistakes fail a pin.
+with a shared expert, and ``layer_w4a8``, are pinned against independent torch
+compositions, and ``tests/test_oracle_mutations.py`` checks that planted mistakes fail
+a pin. ``oracle/w4a4_study.py`` (reading R19, a study of a form the HIP library does not
+compute) is pinned by brute force in ``tests/test_w4a4_study.py``.
 """
 from __future__ import annotations
 

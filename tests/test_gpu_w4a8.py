@@ -306,8 +306,9 @@ class GpuLayerW4A8:
                 bf16_f64(self.n))
 
 
-@pytest.mark.parametrize("name,sample", [("tiny", None), ("decode_t8", None), ("batched_t64", None),
-                                         ("prefill", 1024)])
+# (batched_t64's 256 experts are covered by the FFN step test and by the routing test
+# below, which runs the whole layer at that shape)
+@pytest.mark.parametrize("name,sample", [("tiny", None), ("decode_t8", None), ("prefill", 1024)])
 def test_layer_w4a8(name, sample):
     w = wl.workload(name)
     note(f"w4a8 layer: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} shared={w.n_shared}")

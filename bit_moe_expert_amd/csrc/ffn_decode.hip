@@ -191,7 +191,7 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 // stage whole), each (row, slice) with its own power of two; a slice's partial sums are
 // scaled back before they are added, which keeps the same bits for the same reason.
 template <bool kUp, int D, int kX>
-__global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(1024, 1) void ffn_decode_kernel(DecodeArgs a) {
   constexpr bool kLds = kX != kXRegs;
   constexpr bool kSlice = kX == kXSlice;
   constexpr bool kPerExpert = kX == kXExpert || kSlice;  // workgroup = one expert's pairs
@@ -200,30 +200,52 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar registers)
   const int rn = lane & 15, kq = lane >> 4;
-  const int ksplit = a.ksplit, groups = 4 / ksplit;
+  // 4 waves a workgroup; the all-rows form may run up to 16
+  const int nthr = kX == kXAll ? (int)blockDim.x : 256, nw = nthr >> 6;
+  const int ksplit = a.ksplit, groups = nw / ksplit;
   const int gi = wave / ksplit, q = wave % ksplit;
   const int K = a.K, NS = K / 128, NB = a.N / 16;
   const int pairs_per_group = kUp ? a.I / 16 : a.N / 32;
   // this wave group's unit: spread over dispatch slots, or the workgroup's `groups`
-  // consecutive pairs (of one expert: pairs_per_group is a multiple of 4)
+  // consecutive pairs (of one expert: pairs_per_group is a multiple of 4, and these
+  // forms run 4 waves a workgroup)
   const int b = blockIdx.x, C = a.slots;
   const int unit = kPerExpert ? b * groups + gi : ((b / C) * groups + gi) * C + (b % C);
-  // All-rows form: the first round of the activation copy (8 chunks of 16 bytes per
-  // thread) depends on nothing, so it goes out before the expert lookup and the weight
-  // tiles. Loads return in issue order; issued after the tiles, the copy would wait
-  // for them, and the workgroup's barrier with it.
+  // All-rows form: the activation rows are in LDS before any weight tile is requested.
+  // Their first round (up to 8 chunks of 16 bytes per thread) depends on nothing and
+  // goes out before the expert lookup; the lookup waits for it anyway, so the stores
+  // that follow wait for nothing. Stores placed after the tiles' loads would wait for
+  // the tiles as well (loads return in issue order, and the compiler does not count
+  // loads issued under a condition, so it waits for all): that held every workgroup's
+  // staging, and with it every wave's first step, until the start-up burst of tiles
+  // had arrived (median staging end 6.9 us after entry at T = 8, now 4.7 us).
   constexpr int kU = 8;
   u32x4 pre[kX == kXAll ? kU : 1];
   if constexpr (kX == kXAll) {
     const int cpr = K / 8, total = a.stage_rows * cpr;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int c = u * 256 + tid;
+      const int c = u * nthr + tid;
       const int cc = c < total ? c : 0;
-      pre[u] = reinterpret_cast<const u32x4*>(a.act + (size_t)(cc / cpr) * K)[cc % cpr];
+      if (u * nthr < total) pre[u] = reinterpret_cast<const u32x4*>(a.act + (size_t)(cc / cpr) * K)[cc % cpr];
     }
   }
   const Group grp = find_group(a, unit / pairs_per_group);
+  if constexpr (kX == kXAll) {
+    const int cpr = K / 8, total = a.stage_rows * cpr, xs0 = x_row_stride(K);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = u * nthr + tid;
+      if (c < total) *reinterpret_cast<u32x4*>(smem + (size_t)(c / cpr) * xs0 + (c % cpr) * 16) = pre[u];
+    }
+    // rows beyond the first round (more than 8 chunks a thread), before the tiles too
+    for (int c = kU * nthr + tid; c < total; c += nthr)
+      *reinterpret_cast<u32x4*>(smem + (size_t)(c / cpr) * xs0 + (c % cpr) * 16) =
+          reinterpret_cast<const u32x4*>(a.act + (size_t)(c / cpr) * K)[c % cpr];
+    // Nothing is in flight here; an explicit wait tells the compiler so on every path
+    // (else a later register write behind a skipped store waits for the tiles).
+    __builtin_amdgcn_s_waitcnt(0);
+  }
   const int g = grp.g, r0 = grp.r0, M = grp.M;
   const int pair = unit % pairs_per_group;
   // rows per pass: an MFMA's 16, or the staged rows of the expert form
@@ -306,7 +328,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
     auto store8 = [&](int base, const u32x4* buf) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const int c = base + u * 256 + tid;
+        const int c = base + u * nthr + tid;
         if (c < total) *reinterpret_cast<u32x4*>(smem + (size_t)(c / cpr) * xs + (c % cpr) * 16) = buf[u];
       }
     };
@@ -314,7 +336,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
       u32x4 buf[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const int c = base + u * 256 + tid;
+        const int c = base + u * nthr + tid;
         const int cc = c < total ? c : 0;
         buf[u] = reinterpret_cast<const u32x4*>(a.act + (size_t)srcrow(cc / cpr) * K + k0)[cc % cpr];
       }
@@ -325,7 +347,7 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
       // blocks (lane l's 16 bytes land at block + 16 l), a row's slice being kc / 512
       // of them
       const int bpr = kc / 512;
-      for (int bi = wave; bi < nrows * bpr; bi += 4) {
+      for (int bi = wave; bi < nrows * bpr; bi += nw) {
         const int r = bi / bpr, h = bi % bpr;
         const uint16_t* src = a.act + (size_t)srcrow(r) * K + k0 + h * 512 + lane * 8;
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(smem + (size_t)r * xs + h * 1024),
@@ -335,18 +357,13 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
     } else {
       // the first round outside the loop: a loop head would wait for every load in
       // flight (the weight tiles issued before included) before reusing its registers
-      int base = 0;
-      if constexpr (kX == kXAll) {  // the first round was loaded at the start
-        store8(0, pre);
-        base = kU * 256;
-      } else {
+      if constexpr (kX != kXAll) {  // the all-rows form copied its rows at the start
         copy8(0);
-        base = kU * 256;
+        for (int base = kU * nthr; base < total; base += kU * nthr) copy8(base);
       }
-      for (; base < total; base += kU * 256) copy8(base);
     }
     __syncthreads();
-    for (int row = wave; row < nrows; row += 4) {  // wave w converts rows w, w+4, ...
+    for (int row = wave; row < nrows; row += nw) {  // wave w converts rows w, w+nw, ...
       uint8_t* rp = smem + (size_t)row * xs;
       float mx = 0.f;
       for (int c = lane; c < cpr; c += 64) {
@@ -371,9 +388,9 @@ __global__ __launch_bounds__(256, 4) void ffn_decode_kernel(DecodeArgs a) {
     }
   };
 
-  // Staged forms: pass 0's row index, then its first tiles go out before the
-  // activation copy, so the round trips overlap (the index is waited for only where
-  // it is used, after the copy's loads have been issued)
+  // Staged forms: pass 0's row index, then its first tiles go out, before the
+  // activation copy of the per-expert forms, so the round trips overlap (the index is
+  // waited for only where it is used, after the copy's loads have been issued)
   int src = 0, pair0 = 0;
   if (kLds && npass > 0) {
     pair0 = row_pair(0);
@@ -631,19 +648,27 @@ hipError_t launch(bool up, const DecodeArgs& base, long long active_groups, int 
     }
   }
   a.ksplit = ks;
-  const long long groups_per_wg = 4 / ks;
+  const bool one_round = pairs * ks <= resident_waves(ks);
+  // Waves per workgroup: 4, except for the all-rows form with one wave per pair in a
+  // single round, which takes one workgroup per CU of up to 16 waves, so that each CU
+  // copies and converts the activation rows once instead of once per 4 waves (measured
+  // at T = 8: up 20.9 us against 21.4 us with 4-wave groups).
+  // (The K-split hand-over buffer is sized for 4 waves; it is only used when ks > 1.)
+  int nw = 4;
+  if (mode == kXAll && ks == 1 && one_round)
+    nw = (int)std::min<long long>(16, std::max<long long>(4, (pairs + cus - 1) / cus));
+  const long long groups_per_wg = nw / ks;
   const long long wgs = (pairs + groups_per_wg - 1) / groups_per_wg;
   // a whole number of rounds of `slots` workgroups, so that unit <-> (workgroup,
   // group) is one to one. The spread placement is for grids that are resident at
   // once; larger ones keep consecutive units (the same expert's pairs, whose rows
   // the workgroup's waves share in cache) together (slots = 1). The expert form
   // always takes consecutive units.
-  const bool one_round = pairs * ks <= resident_waves(ks);
   const long long slots = one_round && mode != kXExpert && mode != kXSlice ? std::min<long long>(wgs, cus) : 1;
   a.slots = (int)slots;
   const long long grid = (wgs + slots - 1) / slots * slots;
   const unsigned lds = (unsigned)lds_bytes(ks);
-  const dim3 g3((unsigned)grid), b3(256);
+  const dim3 g3((unsigned)grid), b3((unsigned)(64 * nw));
   if (mode == kXAll) {
     if (up) hipLaunchKernelGGL((ffn_decode_kernel<true, kStagesLds, kXAll>), g3, b3, lds, s, a);
     else hipLaunchKernelGGL((ffn_decode_kernel<false, kStagesLds, kXAll>), g3, b3, lds, s, a);

@@ -232,6 +232,11 @@ FFN_CASES = [
     ("expert8_passes", wl.Workload("expert8_passes", T=48, H=2048, E=128, k=8, I=256, routing="zipf"), None),
     # activations in registers (neither all rows nor one expert's rows fit LDS), several passes
     ("regs_passes", wl.Workload("regs_passes", T=40, H=2048, E=4, k=2, I=256, routing="zipf"), None),
+    # all rows staged, one wave per pair in one round: one workgroup per CU of 8, 11
+    # (2688 pairs, a ragged last round of units) and 16 waves for the up launch
+    ("all_rows_8_waves", wl.Workload("all_rows_8_waves", T=8, H=2048, E=128, k=8, I=512, routing="router"), None),
+    ("all_rows_11_waves", wl.Workload("all_rows_11_waves", T=7, H=2048, E=128, k=8, I=768, routing="router"), None),
+    ("all_rows_16_waves", wl.Workload("all_rows_16_waves", T=8, H=2048, E=128, k=8, I=1024, routing="router"), None),
     # many rows per expert (the MFMA-tile kernel), ragged tails
     ("rows_ragged", wl.Workload("rows_ragged", T=301, H=512, E=8, k=2, I=256, routing="zipf"), None),
     ("prefill_small", wl.Workload("prefill_small", T=1024, H=1024, E=16, k=4, I=384, routing="zipf"), None),

@@ -79,6 +79,22 @@ __device__ __forceinline__ u32x4 dequant8_f16(uint32_t codes, _Float16 s) {
   return r;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in registers: shifts within rows of
+// 16 lanes (lanes shifted in from before the row read 0), then row 0's total added to
+// rows 1 and 3 and rows 0-1's total to rows 2 and 3 (DPP row broadcasts). Every lane
+// of the wave must be active. (Lane shuffles, __shfl_up, go through LDS, one round trip
+// a step: the prefill GEMM's tile schedule, three scans of four rounds of experts, took
+// several microseconds of each workgroup's prologue that way.)
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA wrappers (operand layouts checked on gfx950):
 //  16x16x32 bf16: lane l supplies A[l%16][kslot(l/16, 0..7)], B[kslot(l/16, 0..7)][l%16];

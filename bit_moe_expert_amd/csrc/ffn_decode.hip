@@ -122,12 +122,7 @@ __device__ __forceinline__ Group find_group(const DecodeArgs& a, int j) {
     act[c] = 4 * lane + c < G && v[c + 1] > v[c];
     cnt += act[c] ? 1 : 0;
   }
-  int incl = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const int incl = wave_incl_sum(cnt);
   const int excl = incl - cnt;
   const uint64_t bal = __ballot(j >= excl && j < incl);
   if (bal == 0) return Group{0, 0, 0};

@@ -37,12 +37,7 @@ constexpr int kRoutePlanMaxTokens = 16;
 // by all threads of the block.
 __device__ int block_exclusive_scan256(int v, int* lds4, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const int incl = wave_incl_sum(v);
   if (wave < 4 && lane == 63) lds4[wave] = incl;
   __syncthreads();
   int pre = 0;
@@ -138,12 +133,7 @@ __device__ void plan_wave(const int* flat, int n, int E, int32_t* __restrict__ o
     c[j] = x < E ? start[x] : 0;
     sum += c[j];
   }
-  int incl = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const int incl = wave_incl_sum(sum);
   int pre = incl - sum;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

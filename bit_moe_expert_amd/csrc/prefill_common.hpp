@@ -106,42 +106,36 @@ __device__ __forceinline__ void tile_schedule(const GemmArgs& a, int lane, int* 
       count[c] = cnt;
       int f, t, h;
       classes(cnt, f, t, h);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int of = __shfl_up(f, off), ot = __shfl_up(t, off), oh = __shfl_up(h, off);
-        if (lane >= off) {
-          f += of;
-          t += ot;
-          h += oh;
-        }
-      }
+      f = wave_incl_sum(f);
+      t = wave_incl_sum(t);
+      h = wave_incl_sum(h);
       incl_f[c] = carry_f + f;
       incl_t[c] = carry_t + t;
       incl_h[c] = carry_h + h;
-      carry_f += __shfl(f, 63);
-      carry_t += __shfl(t, 63);
-      carry_h += __shfl(h, 63);
+      carry_f += __builtin_amdgcn_readlane(f, 63);
+      carry_t += __builtin_amdgcn_readlane(t, 63);
+      carry_h += __builtin_amdgcn_readlane(h, 63);
     }
     int q, cls;
     place(carry_f * a.n_tiles, carry_t * a.n_tiles, carry_h * a.n_tiles, q, cls);
     if (q >= 0) {
       const int m = q / a.n_tiles;
       nt = q % a.n_tiles;
-      auto incl_of = [&](int c) { return cls == 0 ? incl_f[c] : (cls == 1 ? incl_t[c] : incl_h[c]); };
 #pragma unroll
       for (int c = 0; c < kMaxExperts / 64; ++c) {
         const int e = 64 * c + lane;
-        const int incl = incl_of(c);
-        const int prev = __shfl_up(incl, 1);  // every lane takes part in both shuffles
-        const int before = c == 0 ? 0 : __shfl(incl_of(c > 0 ? c - 1 : 0), 63);
-        const int excl = lane == 0 ? before : prev;
+        int f, t, h;
+        classes(count[c], f, t, h);
+        const int own = cls == 0 ? f : (cls == 1 ? t : h);
+        const int incl = cls == 0 ? incl_f[c] : (cls == 1 ? incl_t[c] : incl_h[c]);
+        const int excl = incl - own;
         const uint64_t hit = __ballot(e < a.G && m >= excl && m < incl);
         if (hit && g < 0) {
-          const int src = __ffsll((long long)hit) - 1;
-          g = __shfl(e, src);
-          const int mt = cls ? 0 : m - __shfl(excl, src);
-          r0 = __shfl(first[c], src);  // from the counting loads, not a second round trip
-          const int cnt = __shfl(count[c], src);
+          const int src = __ffsll((long long)hit) - 1;  // wave-uniform
+          g = 64 * c + src;
+          const int mt = cls ? 0 : m - __builtin_amdgcn_readlane(excl, src);
+          r0 = __builtin_amdgcn_readlane(first[c], src);  // from the counting loads
+          const int cnt = __builtin_amdgcn_readlane(count[c], src);
           // a three-quarter or half tile is the expert's last M-tile
           const int m0 = cls ? cnt / BM : mt;
           r0 += m0 * BM;

@@ -174,7 +174,14 @@ __device__ __forceinline__ int mxfp8_block(const u32x4 v[4], u32x4 out[2]) {
 // ---------------------------------------------------------------------------
 // Misc
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u in FP32 with the hardware exponential and reciprocal (about 1 ulp each;
+// the result is rounded to BF16, 2^16 times coarser). A correctly rounded division
+// expands to about ten instructions per element, a large share of the GEMM epilogue.
+// 1 + exp(-g) >= 1, so the reciprocal never sees a denormal; -g large gives +inf,
+// whose reciprocal is 0, as the division would give.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 template <typename T>
 __device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }

@@ -68,6 +68,32 @@ __device__ __forceinline__ v8i32 dequant32_fp8(u32x4 c, uint32_t sc) {
   return r;
 }
 
+// The same through a table: for each E4M3 scale byte, the E4M3 bytes of the eight E2M1
+// magnitudes (0, 0.5, 1, 1.5, 2, 3, 4, 6) times that scale, formed once per workgroup
+// by dequant32_fp8 itself (so every byte, saturation included, is the same). A dword of
+// codes (eight weights sharing one scale) then takes two byte permutes for the
+// magnitudes of its even and odd nibbles, the codes' sign bits XOR-ed in (E4M3 and
+// E2M1 both keep the sign in the top bit, and a negative scale's entries carry its
+// sign), and two byte permutes back into element order: about 10 instructions per 8
+// weights instead of 20. (A NaN scale byte, 0x7f or 0xff, gives +-448 by the code's
+// sign.)
+__device__ __forceinline__ v8i32 dequant32_fp8_lut(u32x4 c, uint32_t sc, const uint32_t* tab) {
+  const uint2 t0 = *reinterpret_cast<const uint2*>(tab + 2 * (sc & 0xffu));
+  const uint2 t1 = *reinterpret_cast<const uint2*>(tab + 2 * ((sc >> 8) & 0xffu));
+  v8i32 r;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint2 t = d < 2 ? t0 : t1;
+    const uint32_t w = c[d];
+    // elements 0, 2, 4, 6 (low nibbles) and 1, 3, 5, 7 (high nibbles), one a byte
+    const uint32_t ev = __builtin_amdgcn_perm(t.y, t.x, w & 0x07070707u) ^ ((w << 4) & 0x80808080u);
+    const uint32_t od = __builtin_amdgcn_perm(t.y, t.x, (w >> 4) & 0x07070707u) ^ (w & 0x80808080u);
+    r[2 * d] = (int)__builtin_amdgcn_perm(od, ev, 0x05010400u);      // elements 0..3
+    r[2 * d + 1] = (int)__builtin_amdgcn_perm(od, ev, 0x07030602u);  // elements 4..7
+  }
+  return r;
+}
+
 __device__ __forceinline__ f32x16 mfma_fp8(v8i32 a, v8i32 b, int sa, f32x16 c) {
   // A and B both E4M3 (format 0); A block scale sa (E8M0), B scale 2^0 (127)
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, 127);
@@ -87,9 +113,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_fp8_kernel(GemmArgs a
   __shared__ __attribute__((aligned(16))) uint8_t ldsb1[4 * kBWave8];
   __shared__ __attribute__((aligned(16))) uint8_t ldsb2[4 * kBWave8];
   __shared__ int sched[4];
+  __shared__ __attribute__((aligned(16))) uint32_t ldst[2 * 256];  // E4M3 table per scale byte
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (wave == 0) tile_schedule<kDense>(a, lane, sched);
+  {  // thread t forms the table entry of scale byte t: codes 0..7 (magnitudes) times it
+    const v8i32 e = dequant32_fp8(u32x4{0x76543210u, 0u, 0u, 0u}, (uint32_t)tid | ((uint32_t)tid << 8));
+    *reinterpret_cast<uint2*>(&ldst[2 * tid]) = make_uint2((uint32_t)e[0], (uint32_t)e[1]);
+  }
   __syncthreads();
   const int g = sched[0];
   if (g < 0) return;
@@ -224,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_fp8_kernel(GemmArgs a
         const auto s1 = __builtin_amdgcn_permlane32_swap(c[1], c[3], false, false);
         const u32x4 cs = {s0[0], s1[0], s0[1], s1[1]};
         const auto ss = __builtin_amdgcn_permlane32_swap(sc, sc, false, false);
-        Bv[j] = dequant32_fp8(cs, __builtin_amdgcn_perm(ss[1], ss[0], ssel));
+        Bv[j] = dequant32_fp8_lut(cs, __builtin_amdgcn_perm(ss[1], ss[0], ssel), ldst);
       }
     };
     constexpr int kAfter = MI + 7;  // one step's copies: MI rows, 1 scale, 4 codes, 2 scales

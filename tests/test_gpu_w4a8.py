@@ -198,7 +198,8 @@ def test_expert_ffn_w4a8_tile_edges():
 def test_expert_ffn_w4a8_weight_extremes_and_wide_rows():
     """Weights whose code * scale leaves E4M3's range at both ends: block scales up to
     448 (6 * 448 = 2688 saturates to 448; 4 * 128 = 512 too) and down to E4M3's
-    smallest subnormal 2^-9 (0.5 * 2^-9 rounds to 0, ties to even), non-unit tensor
+    smallest subnormal 2^-9 (0.5 * 2^-9 rounds to 0, ties to even), half of them
+    negative (a negative code times a negative scale is positive), non-unit tensor
     scales, and activation rows of very different magnitudes (2^-40 .. 2^20, each
     value within 2^-20 of its row's largest; h grows as the square of x, so larger
     rows would leave FP32) with zero blocks. Checked against the summation bound
@@ -212,6 +213,7 @@ def test_expert_ffn_w4a8_weight_extremes_and_wide_rows():
         u = rng.uniform(-12, 9, m.scales.shape)
         m.scales[:] = wl.to_e4m3_codes(np.minimum(np.exp2(u), 448.0))
         m.scales[m.scales == 0x7f] = 0x7e
+        m.scales[:] |= (rng.random(m.scales.shape) < 0.5).astype(np.uint8) << 7  # sign bit
         m.tscale[:] = rng.uniform(0.25, 2.0, m.tscale.shape).astype(np.float32)
     row_scale = np.exp2(rng.uniform(-40, 20, (inp.T, 1)))
     xv = rng.standard_normal((inp.T, w.H)) * np.exp2(rng.uniform(-20, 0, (inp.T, w.H))) * row_scale
@@ -219,6 +221,7 @@ def test_expert_ffn_w4a8_weight_extremes_and_wide_rows():
     inp.x[:] = wl.to_bf16_bits(xv)
     W13 = oracle.dequant(inp.w13.packed[0], inp.w13.scales[0], 1.0)
     assert np.any(np.abs(W13) > 448) and np.any((W13 != 0) & (np.abs(W13) < 2.0 ** -9))
+    assert np.any(oracle.e4m3_value(inp.w13.scales[0]) < 0)
     idx, _, off, perm, inv = _plan_on_host(inp)
     h_bits, y_bits = _run_w4a8_ffn(inp, w, off, perm)
     got_h, got_y = oracle.bf16_value(h_bits), oracle.bf16_value(y_bits)

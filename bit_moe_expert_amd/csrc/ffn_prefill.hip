@@ -325,13 +325,21 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 16; r += 2) {
+        // rows lr and lr + 1 of column r32: one packed conversion, two 16-bit stores
         const int lr = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
         if (kUp) {
-          stage[lr * W + r32] = f32_to_bf16(silu_mul(ts * acc[i][0][r], ts * acc[i][1][r]));
+          const uint32_t p = pack_bf16x2(silu_mul(ts * acc[i][0][r], ts * acc[i][1][r]),
+                                         silu_mul(ts * acc[i][0][r + 1], ts * acc[i][1][r + 1]));
+          stage[lr * W + r32] = (uint16_t)p;
+          stage[(lr + 1) * W + r32] = (uint16_t)(p >> 16);
         } else {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) stage[lr * W + 32 * j + r32] = f32_to_bf16(ts * acc[i][j][r]);
+          for (int j = 0; j < 2; ++j) {
+            const uint32_t p = pack_bf16x2(ts * acc[i][j][r], ts * acc[i][j][r + 1]);
+            stage[lr * W + 32 * j + r32] = (uint16_t)p;
+            stage[(lr + 1) * W + 32 * j + r32] = (uint16_t)(p >> 16);
+          }
         }
       }
     }

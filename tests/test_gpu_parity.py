@@ -368,6 +368,28 @@ def test_expert_ffn_wide_range_rows(name):
                               min_equal=0.8)
 
 
+SIGNED_SCALE_CASES = ["decode_t8", "regs_passes", "expert_staged", "rows_ragged", "prefill_small"]
+
+
+@pytest.mark.parametrize("name", SIGNED_SCALE_CASES)
+def test_expert_ffn_signed_block_scales(name):
+    """Block scales of both signs over a wider range (E4M3 codes with the sign bit set
+    half the time, magnitudes 2^-6 .. 2^6): a negative code times a negative scale is
+    positive in every dequantisation form (the streaming kernel's BF16 and FP16 forms,
+    the GEMM's BF16 one; tiled and canonical layouts). Checked as the routed cases
+    are."""
+    w = dict((c[0], c[1]) for c in FFN_CASES)[name] or wl.workload(name)
+    note(f"expert ffn signed block scales: {name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I}")
+    inp = wl.make_inputs(w, seed=12)
+    rng = np.random.default_rng(121)
+    for m in (inp.w13, inp.w2):
+        m.scales[:] = wl.to_e4m3_codes(np.exp2(rng.uniform(-6, 6, m.scales.shape)))
+        m.scales[:] |= (rng.random(m.scales.shape) < 0.5).astype(np.uint8) << 7  # sign bit
+    assert np.any(oracle.e4m3_value(inp.w13.scales) < 0) and np.any(oracle.e4m3_value(inp.w13.scales) > 0)
+    idx, _, off, perm, inv = _plan_on_host(inp)
+    _check_routed_ffn(inp, w, off, perm)
+
+
 @pytest.mark.parametrize("T", [1, 8, 17, 39, 77, 200, 300])
 def test_expert_ffn_dense_shared(T):
     """Dense (shared expert) mode: on the streaming kernel below 40 rows (1, 8, 17 and

@@ -117,6 +117,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_fp8_kernel(GemmArgs a
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (wave == 0) tile_schedule<kDense>(a, lane, sched);
+  static_assert(kThreads == 256, "one thread per table entry (scale byte)");
   {  // thread t forms the table entry of scale byte t: codes 0..7 (magnitudes) times it
     const v8i32 e = dequant32_fp8(u32x4{0x76543210u, 0u, 0u, 0u}, (uint32_t)tid | ((uint32_t)tid << 8));
     *reinterpret_cast<uint2*>(&ldst[2 * tid]) = make_uint2((uint32_t)e[0], (uint32_t)e[1]);

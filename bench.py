@@ -484,6 +484,18 @@ def main():
     # so the mean is the kernel's own duration plus the gap between launches, not the
     # events' overhead. The routed up launch (pass 2) is the dominant kernel.
     pairs = T * w.k
+    # where the up projections run on the GEMM, moe4_layer takes them on FP16 activations
+    # (moe4_act_f16 once per call, then moe4_expert_up_f16): time the same launches
+    prefill_routed = T * w.k >= 40 * w.E and w.H % 256 == 0 and w.I % 128 == 0
+    prefill_dense = T >= 40 and w.H % 256 == 0 and w.I % 128 == 0
+    f16_act = not fp8 and (prefill_routed or (s13 is not None and prefill_dense))
+
+    def up_call(shp, c, offsets, perm_src, a13, h, gemm):
+        if f16_act and gemm:
+            B.moe4_expert_up_f16(shp, c["x16"], c["xexp"], offsets, perm_src, a13, h)
+        else:
+            B.moe4_expert_up(shp, c["x"], offsets, perm_src, a13, h)
+
     pws_n = B.moe4_permute_workspace_bytes(shape)
     pws = torch.empty(pws_n, dtype=torch.uint8, device="cuda") if pws_n else None
     plans, routing, hs, hds = [], [], [], []
@@ -503,7 +515,11 @@ def main():
             B.moe4_expert_up_w4a8(shape, c["x8"], c["xs"], offsets, perm_src, w13, None, *h)
         else:
             h = torch.empty((pairs, w.I), dtype=torch.int16, device="cuda")
-            B.moe4_expert_up(shape, c["x"], offsets, perm_src, w13, h)
+            if f16_act:  # as moe4_layer does where its up projections run on the GEMM
+                c["x16"] = torch.empty((T, w.H), dtype=torch.float16, device="cuda")
+                c["xexp"] = torch.empty(T, dtype=torch.int32, device="cuda")
+                B.moe4_act_f16(c["x"], c["x16"], c["xexp"])
+            up_call(shape, c, offsets, perm_src, w13, h, prefill_routed)
         hs.append(h)
         if s13 is not None:
             if fp8:
@@ -511,7 +527,7 @@ def main():
                 B.moe4_expert_up_w4a8(shape, c["x8"], c["xs"], None, None, s13, None, *hd)
             else:
                 hd = torch.empty((T, w.I), dtype=torch.int16, device="cuda")
-                B.moe4_expert_up(shape, c["x"], None, None, s13, hd)
+                up_call(shape, c, None, None, s13, hd, prefill_dense)
             hds.append(hd)
         torch.cuda.synchronize()
         routing.append(topk_idx.cpu().numpy())
@@ -528,7 +544,7 @@ def main():
         if fp8:
             B.moe4_expert_up_w4a8(shape, c["x8"], c["xs"], offsets, perm_src, a13, None, *h_tmp)
         else:
-            B.moe4_expert_up(shape, c["x"], offsets, perm_src, a13, h_tmp)
+            up_call(shape, c, offsets, perm_src, a13, h_tmp, prefill_routed)
 
     def down_routed(i):
         offsets, _ = plans[i % chunks]
@@ -543,7 +559,7 @@ def main():
         if fp8:
             B.moe4_expert_up_w4a8(shape, c["x8"], c["xs"], None, None, s13, None, *hd_tmp)
         else:
-            B.moe4_expert_up(shape, c["x"], None, None, s13, hd_tmp)
+            up_call(shape, c, None, None, s13, hd_tmp, prefill_dense)
 
     def down_shared(i):
         if fp8:
@@ -577,8 +593,13 @@ def main():
             fl += f
         nb /= chunks
         fl /= chunks
-        kernels[name] = {"kernel": f"{kind_name}<{str(up).lower()}, {str(dense).lower()}>"
-                                   if prefill_kind else f"{kind_name}<{str(up).lower()}, ...>",
+        if up and f16_act and (prefill_dense if dense else prefill_routed):
+            kname = f"ffn_prefill_f16_kernel<{str(dense).lower()}, true>"
+        elif prefill_kind:
+            kname = f"{kind_name}<{str(up).lower()}, {str(dense).lower()}>"
+        else:
+            kname = f"{kind_name}<{str(up).lower()}, ...>"
+        kernels[name] = {"kernel": kname,
                          "mean_us": round(mean_s * 1e6, 3), "launches": k2 * chunks,
                          "algorithmic_bytes": int(nb), "algorithmic_flops": int(fl),
                          "GB_s": round(nb / mean_s / 1e9, 1), "TFLOP_s": round(fl / mean_s / 1e12, 1)}
@@ -586,11 +607,31 @@ def main():
             f"launches; {nb / 1e6:.1f} MB, {fl / 1e9:.2f} GFLOP per launch -> {nb / mean_s / 1e9:.0f} GB/s, "
             f"{fl / mean_s / 1e12:.1f} TFLOP/s")
 
+    # the FP16 activation rows (once per layer call, before the up GEMMs), timed the same way
+    if f16_act:
+        for i in range(min(k2, 10) * chunks):
+            c = per_chunk[i % chunks]
+            B.moe4_act_f16(c["x"], c["x16"], c["xexp"])
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(k2 * chunks):
+            c = per_chunk[i % chunks]
+            B.moe4_act_f16(c["x"], c["x16"], c["xexp"])
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        mean_s = ev0.elapsed_time(ev1) / (k2 * chunks) / 1e3
+        nb = 2 * T * w.H * 2 + T * 4
+        kernels["act_f16"] = {"kernel": "act_f16_kernel (FP16 activation rows for the up GEMMs)",
+                              "mean_us": round(mean_s * 1e6, 3), "launches": k2 * chunks,
+                              "algorithmic_bytes": int(nb), "GB_s": round(nb / mean_s / 1e9, 1)}
+        log(f"pass 3: act_f16 mean {mean_s * 1e6:.2f} us; {nb / 1e6:.1f} MB -> {nb / mean_s / 1e9:.0f} GB/s")
+
     # the expert FFN as a whole: every FFN launch of a layer call (both GEMMs, routed and
-    # shared), total work over total time
+    # shared, and the FP16 activation rows where the layer makes them), total work over
+    # total time
     tot_us = sum(v["mean_us"] for v in kernels.values())
     tot_b = sum(v["algorithmic_bytes"] for v in kernels.values())
-    tot_f = sum(v["algorithmic_flops"] for v in kernels.values())
+    tot_f = sum(v.get("algorithmic_flops", 0) for v in kernels.values())
     kernels["ffn_total"] = {"kernel": "every expert-FFN launch of a layer call", "mean_us": round(tot_us, 3),
                             "algorithmic_bytes": int(tot_b), "algorithmic_flops": int(tot_f),
                             "GB_s": round(tot_b / tot_us / 1e3, 1), "TFLOP_s": round(tot_f / tot_us / 1e6, 1)}

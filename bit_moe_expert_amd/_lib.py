@@ -51,6 +51,8 @@ SIGNATURES = {
     "moe4_expert_ffn": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, _W4, _W4, c_void_p, c_void_p,
                                 c_void_p]),
     "moe4_expert_up": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, _W4, c_void_p, c_void_p]),
+    "moe4_act_f16": (c_int, [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe4_expert_up_f16": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, c_void_p, _W4, c_void_p, c_void_p]),
     "moe4_expert_down": (c_int, [_SHAPE, c_void_p, c_void_p, _W4, c_void_p, c_void_p]),
     "moe4_combine_norm": (c_int, [_SHAPE, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_void_p]),

@@ -16,6 +16,7 @@ from . import _lib
 from ._lib import Shape, W4, check
 
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+_F16_LIKE = (torch.float16, torch.int16, torch.uint16)
 
 
 def _ptr(t: Optional[torch.Tensor], name: str, dtypes=None, numel: Optional[int] = None):
@@ -135,6 +136,24 @@ def moe4_expert_up(shape: Shape, x, offsets, perm_src, w13: DeviceW4, h, stream=
     d13 = w13.desc()
     check(_lib.load().moe4_expert_up(
         shape, _ptr(x, "x", _BF16_LIKE, shape.T * shape.H),
+        _ptr(offsets, "offsets", (torch.int32,)), _ptr(perm_src, "perm_src", (torch.int32,)),
+        d13, _ptr(h, "h", _BF16_LIKE, rows * shape.I), _stream(stream)))
+
+
+def moe4_act_f16(x, x16, xexp, stream=None) -> None:
+    """FP16 rows of BF16 x [rows][K], each scaled by its own power of two: x16
+    [rows][K] (float16 or 16-bit storage), xexp int32 [rows]."""
+    rows, K = x.shape
+    check(_lib.load().moe4_act_f16(
+        rows, K, _ptr(x, "x", _BF16_LIKE), _ptr(x16, "x16", _F16_LIKE, rows * K),
+        _ptr(xexp, "xexp", (torch.int32,), rows), _stream(stream)))
+
+
+def moe4_expert_up_f16(shape: Shape, x16, xexp, offsets, perm_src, w13: DeviceW4, h, stream=None) -> None:
+    rows = shape.T * shape.k if offsets is not None else shape.T
+    d13 = w13.desc()
+    check(_lib.load().moe4_expert_up_f16(
+        shape, _ptr(x16, "x16", _F16_LIKE, shape.T * shape.H), _ptr(xexp, "xexp", (torch.int32,), shape.T),
         _ptr(offsets, "offsets", (torch.int32,)), _ptr(perm_src, "perm_src", (torch.int32,)),
         d13, _ptr(h, "h", _BF16_LIKE, rows * shape.I), _stream(stream)))
 

@@ -9,6 +9,11 @@
 #include "../../include/moe4.h"
 #include "launch.hpp"
 
+namespace moe4 {
+// whether the up projection of a call runs on the MFMA GEMM (defined below)
+bool up_uses_gemm(const int32_t* offsets, int T, int k, int G, int H, int I);
+}  // namespace moe4
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -81,13 +86,19 @@ moe4::W4View view(const moe4_w4* w) {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct LayerWs {
-  size_t offsets, perm_src, inv, perm_ws, h, y, total;
+  size_t offsets, perm_src, inv, perm_ws, h, y, x16, xexp, total;
+  bool f16;  // the layer's up GEMMs take FP16 activations (x16, xexp)
 };
 
+// The layer's up projections that run on the MFMA GEMM take the activations in FP16
+// (moe4_act_f16's form, computed once per call into the workspace).
 LayerWs layer_ws_layout(const moe4_shape* s) {
   LayerWs l{};
   const size_t pairs = (size_t)s->T * s->k;
   const size_t rows = pairs + (size_t)s->T * s->n_shared;
+  const int32_t plan = 1;  // any non-NULL offsets: the routed call
+  l.f16 = moe4::up_uses_gemm(&plan, s->T, s->k, s->E, s->H, s->I) ||
+          (s->n_shared && moe4::up_uses_gemm(nullptr, s->T, s->k, 1, s->H, s->I));
   size_t o = 0;
   l.offsets = o; o += align256((size_t)(s->E + 1) * 4);
   l.perm_src = o; o += align256(pairs * 4);
@@ -95,6 +106,10 @@ LayerWs layer_ws_layout(const moe4_shape* s) {
   l.perm_ws = o;  o += align256(moe4::permute_workspace_bytes((long long)pairs, s->E));
   l.h = o;        o += align256(rows * s->I * 2);
   l.y = o;        o += align256(rows * s->H * 2);
+  if (l.f16) {
+    l.x16 = o;    o += align256((size_t)s->T * s->H * 2);
+    l.xexp = o;   o += align256((size_t)s->T * 4);
+  }
   l.total = o;
   return l;
 }
@@ -173,6 +188,10 @@ static bool use_prefill(const int32_t* offsets, int T, int k, int G, int H, int 
   if (!prefill_shape_ok(H, I)) return false;
   const long long rows = offsets ? (long long)T * k : T;
   return rows >= kPrefillRowsPerExpert * (offsets ? G : 1);
+}
+
+bool up_uses_gemm(const int32_t* offsets, int T, int k, int G, int H, int I) {
+  return use_prefill(offsets, T, k, G, H, I);
 }
 
 hipError_t launch_ffn_up(const uint16_t* x, const int32_t* offsets, const int32_t* perm_src, int k,
@@ -342,6 +361,50 @@ moe4_status moe4_expert_down(const moe4_shape* shape, const uint16_t* h, const i
   return MOE4_OK;
 }
 
+moe4_status moe4_act_f16(int64_t rows, int32_t K, const uint16_t* x, uint16_t* x16, int32_t* xexp,
+                         void* stream) {
+  g_err[0] = 0;
+  if (rows < 0 || K <= 0) return fail(MOE4_ERR_INVALID_ARG, "negative or zero size (rows=%lld K=%d)", (long long)rows, K);
+  if (K % 8 || K > 16384) return fail(MOE4_ERR_UNSUPPORTED, "K=%d must be a multiple of 8, at most 16384", K);
+  if (rows >= (1LL << 31)) return fail(MOE4_ERR_UNSUPPORTED, "rows=%lld >= 2^31", (long long)rows);
+  if (rows == 0) return MOE4_OK;
+  NEED(x, "x");
+  NEED(x16, "x16");
+  if (xexp == nullptr) return fail(MOE4_ERR_INVALID_ARG, "xexp is NULL");
+  if (reinterpret_cast<uintptr_t>(xexp) & 3u) return fail(MOE4_ERR_INVALID_ARG, "xexp is not 4-byte aligned");
+  hipError_t e = moe4::launch_act_f16(x, rows, K, x16, xexp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "act_f16 launch");
+  return MOE4_OK;
+}
+
+moe4_status moe4_expert_up_f16(const moe4_shape* shape, const uint16_t* x16, const int32_t* xexp,
+                               const int32_t* offsets, const int32_t* perm_src, const moe4_w4* w13,
+                               uint16_t* h, void* stream) {
+  g_err[0] = 0;
+  moe4_status st = check_shape(shape);
+  if (st) return st;
+  if (!moe4::prefill_shape_ok(shape->H, shape->I))
+    return fail(MOE4_ERR_UNSUPPORTED, "the GEMM form needs H %% 256 == 0 and I %% 128 == 0 (H=%d I=%d)", shape->H,
+                shape->I);
+  if (shape->T == 0) return MOE4_OK;  // nothing to read or write
+  if ((offsets == nullptr) != (perm_src == nullptr))
+    return fail(MOE4_ERR_INVALID_ARG, "offsets and perm_src must both be set or both be NULL");
+  NEED(x16, "x16");
+  if (xexp == nullptr) return fail(MOE4_ERR_INVALID_ARG, "xexp is NULL");
+  if (reinterpret_cast<uintptr_t>(xexp) & 3u) return fail(MOE4_ERR_INVALID_ARG, "xexp is not 4-byte aligned");
+  if (offsets) {
+    NEED(offsets, "offsets");
+    NEED(perm_src, "perm_src");
+  }
+  if ((st = check_w4(w13, "w13"))) return st;
+  NEED(h, "h");
+  const int G = offsets ? shape->E : 1;
+  hipError_t e = moe4::launch_ffn_up_prefill_f16(x16, xexp, offsets, perm_src, shape->k, shape->T, G, shape->H,
+                                                 shape->I, view(w13), h, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ffn up (FP16 activations) launch");
+  return MOE4_OK;
+}
+
 moe4_status moe4_combine_norm(const moe4_shape* shape, const uint16_t* y, const int32_t* inv,
                               const float* topk_w, const uint16_t* shared_y,
                               const uint16_t* residual, const uint16_t* gamma,
@@ -464,8 +527,21 @@ static moe4_status layer_impl(const moe4_shape* shape, const uint16_t* x, const 
   // stays on the main stream, which then waits for the chain before the combine)
   hipStream_t s = two_streams ? static_cast<hipStream_t>(side_stream) : main;
   const int T = shape->T, H = shape->H, E = shape->E, k = shape->k, I = shape->I;
+  uint16_t* x16 = L.f16 ? reinterpret_cast<uint16_t*>(base + L.x16) : nullptr;
+  int32_t* xexp = L.f16 ? reinterpret_cast<int32_t*>(base + L.xexp) : nullptr;
 
   hipError_t e;
+  if (L.f16) {  // before the fork: both streams' up GEMMs read it
+    e = moe4::launch_act_f16(x, T, H, x16, xexp, main);
+    if (e != hipSuccess) return hip_fail(e, "act_f16 launch");
+  }
+  // the up projection: the GEMM on FP16 activations where the GEMM runs
+  auto up = [&](const int32_t* offs, const int32_t* psrc, int G, const moe4_w4* w, uint16_t* hh,
+                hipStream_t st) {
+    if (L.f16 && moe4::up_uses_gemm(offs, T, k, G, H, I))
+      return moe4::launch_ffn_up_prefill_f16(x16, xexp, offs, psrc, k, T, G, H, I, view(w), hh, st);
+    return moe4::launch_ffn_up(x, offs, psrc, k, T, G, H, I, view(w), hh, st);
+  };
   if (two_streams) {
     e = hipEventRecord(static_cast<hipEvent_t>(fork_event), main);
     if (e != hipSuccess) return hip_fail(e, "fork event record");
@@ -485,7 +561,7 @@ static moe4_status layer_impl(const moe4_shape* shape, const uint16_t* x, const 
     e = moe4::launch_permute(topk_idx, (long long)pairs, E, offsets, perm_src, inv, perm_ws, s);
     if (e != hipSuccess) return hip_fail(e, "permute launch");
   }
-  e = moe4::launch_ffn_up(x, offsets, perm_src, k, T, E, H, I, view(w13), h, s);
+  e = up(offsets, perm_src, E, w13, h, s);
   if (e != hipSuccess) return hip_fail(e, "ffn up launch");
   e = moe4::launch_ffn_down(h, offsets, k, T, E, H, I, view(w2), y, s);
   if (e != hipSuccess) return hip_fail(e, "ffn down launch");
@@ -493,7 +569,7 @@ static moe4_status layer_impl(const moe4_shape* shape, const uint16_t* x, const 
   if (shape->n_shared) {
     uint16_t* hs = h + pairs * I;
     uint16_t* ys = y + pairs * H;
-    e = moe4::launch_ffn_up(x, nullptr, nullptr, k, T, 1, H, I, view(shared13), hs, main);
+    e = up(nullptr, nullptr, 1, shared13, hs, main);
     if (e != hipSuccess) return hip_fail(e, "shared ffn up launch");
     e = moe4::launch_ffn_down(hs, nullptr, k, T, 1, H, I, view(shared2), ys, main);
     if (e != hipSuccess) return hip_fail(e, "shared ffn down launch");

@@ -53,6 +53,12 @@ using namespace prefill;
 
 constexpr int kBWave = 2 * 1024 + 2 * 256;  // weight bytes one wave copies per K step
 
+// 32x32x16 FP16 MFMA (operands in the lanes and slots of the BF16 one)
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+
 // One wave's weight operands of a K step, read from its LDS slot: the 16 code bytes
 // of each of its two 32-row blocks and the dword holding their two E4M3 scales.
 struct WRaw {
@@ -64,8 +70,14 @@ struct WRaw {
 // groups of the plan. (Separate instantiations, so that a kernel trace lists the
 // routed and the shared launches apart.) kTiled: the weights' layout (tiled, else
 // canonical); a compile-time choice, so the tiled form's addressing stays shifts.
-template <bool kUp, bool kDense, bool kTiled>
-__global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
+// kF16 (up only): the activations are FP16 rows scaled by a power of two each (act =
+// x * 2^-xexp[token]); the weights are dequantised into FP16 (two instructions per
+// pair of weights instead of four) and multiplied by FP16 MFMAs, and the epilogue
+// scales each row's FP32 sums back by 2^xexp. Every product is exact in both forms and
+// a power-of-two scale scales every FP32 partial sum exactly, so h has the BF16 form's
+// bits while the row's values are exact in FP16.
+template <bool kUp, bool kDense, bool kTiled, bool kF16>
+__device__ __forceinline__ void prefill_gemm(const GemmArgs& a) {
   // three activation buffers [256][64] BF16 (the ring of steps st, st+1, st+2) and a
   // fourth one for the epilogue's staging; separate arrays, so that the compiler can
   // tell a direct-to-LDS copy into one from reads of another
@@ -79,6 +91,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ldsb1[4 * kBWave];
   __shared__ __attribute__((aligned(16))) uint8_t ldsb2[4 * kBWave];
   __shared__ int sched[4];
+  // kF16: the tile's per-row exponents (row r's token's xexp), copied in at the start
+  __shared__ __attribute__((aligned(16))) int32_t rexp[kF16 ? BM : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -88,6 +102,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   if (g < 0) return;
   const int nt = sched[3];
   const int row0 = sched[1], rows = sched[2];
+  // the token of tile row tid (rows past the tile's end take its first row)
+  int rexp_tok = 0;
+  if constexpr (kF16) {
+    rexp_tok = row0 + (tid < rows ? tid : 0);
+    if (!kDense) rexp_tok = a.perm_src[rexp_tok] / a.k;
+  }
 
   const int K = a.K, NS = K / 128, NB = a.N / 16, nsteps = K / BK;
   const float ts = a.tscale[g];
@@ -199,8 +219,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
     auto deq_b = [&](const WRaw& r, int s, u32x4* Bv) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float sc = s < 2 ? e4m3_to_f32<0>(r.s[j]) : e4m3_to_f32<1>(r.s[j]);
-        Bv[j] = dequant8(r.c[j][s], sc);
+        if constexpr (kF16) {
+          const f16x2 sc2 = e4m3x2_to_f16(r.s[j]);
+          Bv[j] = dequant8_f16(r.c[j][s], s < 2 ? sc2[0] : sc2[1]);
+        } else {
+          const float sc = s < 2 ? e4m3_to_f32<0>(r.s[j]) : e4m3_to_f32<1>(r.s[j]);
+          Bv[j] = dequant8(r.c[j][s], sc);
+        }
       }
     };
     // s_waitcnt vmcnt(MI + 4) lgkmcnt(0): at most one step's copies (MI activation
@@ -221,6 +246,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
     load_b(0, bbuf_of(C0{}));
     load_a(min(1, nsteps - 1), buf_of(C1{}));
     load_b(min(1, nsteps - 1), bbuf_of(C1{}));
+    // kF16: the row exponents, one 4-byte copy per thread (issued after the first two
+    // steps' copies, so the waits below count them as part of step 1; they have landed
+    // by the epilogue's wait for everything)
+    if constexpr (kF16)
+      __builtin_amdgcn_global_load_lds(a.xexp + rexp_tok, (__attribute__((address_space(3))) void*)&rexp[64 * wv], 4,
+                                       0, 0);
     __builtin_amdgcn_s_waitcnt(kWait);
     asm volatile("s_barrier" ::: "memory");
     read_b(C0{}, raw);
@@ -266,7 +297,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+          for (int j = 0; j < 2; ++j) {
+            if constexpr (kF16) acc[i][j] = mfma32x32x16_f16(fa[i], fb[j], acc[i][j]);
+            else acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+          }
         if (s + 1 < BK / 16) {
 #pragma unroll
           for (int g2 = 0; g2 < MI; ++g2) {
@@ -328,7 +362,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
       for (int r = 0; r < 16; r += 2) {
         // rows lr and lr + 1 of column r32: one packed conversion, two 16-bit stores
         const int lr = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (kUp) {
+        if constexpr (kF16) {
+          // this row pair's exponents (rows lr, lr + 1 of the tile)
+          const int e0 = rexp[lr], e1 = rexp[lr + 1];
+          const uint32_t p = pack_bf16x2(
+              silu_mul(__builtin_ldexpf(ts * acc[i][0][r], e0), __builtin_ldexpf(ts * acc[i][1][r], e0)),
+              silu_mul(__builtin_ldexpf(ts * acc[i][0][r + 1], e1), __builtin_ldexpf(ts * acc[i][1][r + 1], e1)));
+          stage[lr * W + r32] = (uint16_t)p;
+          stage[(lr + 1) * W + r32] = (uint16_t)(p >> 16);
+        } else if (kUp) {
           const uint32_t p = pack_bf16x2(silu_mul(ts * acc[i][0][r], ts * acc[i][1][r]),
                                          silu_mul(ts * acc[i][0][r + 1], ts * acc[i][1][r + 1]));
           stage[lr * W + r32] = (uint16_t)p;
@@ -362,9 +404,30 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
   else compute(std::integral_constant<int, 8>{});
 }
 
+template <bool kUp, bool kDense, bool kTiled>
+__global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(GemmArgs a) {
+  prefill_gemm<kUp, kDense, kTiled, false>(a);
+}
+// the FP16-activation form of the up projection (its own name in kernel traces)
+template <bool kDense, bool kTiled>
+__global__ __launch_bounds__(kThreads, 1) void ffn_prefill_f16_kernel(GemmArgs a) {
+  prefill_gemm<true, kDense, kTiled, true>(a);
+}
+
 hipError_t launch(bool up, GemmArgs a, long long m_tiles, hipStream_t s) {
   const dim3 g = size_grid(a, up, m_tiles), b(kThreads);
   const bool dense = a.offsets == nullptr;
+  if (a.xexp) {
+    if (!up) return hipErrorInvalidValue;
+    if (a.tiled) {
+      if (!dense) hipLaunchKernelGGL((ffn_prefill_f16_kernel<false, true>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((ffn_prefill_f16_kernel<true, true>), g, b, 0, s, a);
+    } else {
+      if (!dense) hipLaunchKernelGGL((ffn_prefill_f16_kernel<false, false>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((ffn_prefill_f16_kernel<true, false>), g, b, 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (a.tiled) {
     if (!dense && up) hipLaunchKernelGGL((ffn_prefill_kernel<true, false, true>), g, b, 0, s, a);
     if (!dense && !up) hipLaunchKernelGGL((ffn_prefill_kernel<false, false, true>), g, b, 0, s, a);
@@ -389,6 +452,15 @@ hipError_t launch_ffn_up_prefill(const uint16_t* x, const int32_t* offsets, cons
   if (T == 0) return hipSuccess;
   GemmArgs a{x, offsets, perm_src, k, T, w13.packed, w13.scales, w13.tscale, 2 * I, H, I, G, h, 0, 0,
              w13.tiled ? 1 : 0, nullptr, nullptr, nullptr, nullptr};
+  return launch(true, a, m_tile_bound(offsets, T, k, G), s);
+}
+
+hipError_t launch_ffn_up_prefill_f16(const uint16_t* x16, const int32_t* xexp, const int32_t* offsets,
+                                     const int32_t* perm_src, int k, int T, int G, int H, int I, W4View w13,
+                                     uint16_t* h, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  GemmArgs a{x16, offsets, perm_src, k, T, w13.packed, w13.scales, w13.tscale, 2 * I, H, I, G, h, 0, 0,
+             w13.tiled ? 1 : 0, nullptr, nullptr, nullptr, nullptr, xexp};
   return launch(true, a, m_tile_bound(offsets, T, k, G), s);
 }
 

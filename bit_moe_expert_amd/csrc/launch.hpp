@@ -55,6 +55,13 @@ hipError_t launch_ffn_up_prefill(const uint16_t* x, const int32_t* offsets, cons
                                  int T, int G, int H, int I, W4View w13, uint16_t* h, hipStream_t s);
 hipError_t launch_ffn_down_prefill(const uint16_t* h, const int32_t* offsets, int k, int T, int G, int H,
                                    int I, W4View w2, uint16_t* y, hipStream_t s);
+// FP16-activation form of the up GEMM: x16 [T][H] = x * 2^-xexp[t] in FP16 (from
+// launch_act_f16); the same h as launch_ffn_up_prefill while x16 holds x exactly.
+hipError_t launch_ffn_up_prefill_f16(const uint16_t* x16, const int32_t* xexp, const int32_t* offsets,
+                                     const int32_t* perm_src, int k, int T, int G, int H, int I, W4View w13,
+                                     uint16_t* h, hipStream_t s);
+// x [rows][K] BF16 -> x16 [rows][K] FP16 and xexp [rows] (K % 8 == 0, K <= 16384)
+hipError_t launch_act_f16(const uint16_t* x, long long rows, int K, uint16_t* x16, int32_t* xexp, hipStream_t s);
 
 // FP8 (W4A8) prefill form: activations as block-scaled E4M3 (32 values per E8M0
 // scale), weights rounded to E4M3, block-scaled FP8 MFMAs. x [rows][K] BF16 ->

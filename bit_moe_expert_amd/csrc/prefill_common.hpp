@@ -37,6 +37,8 @@ struct GemmArgs {
   const uint8_t* ascale;    // their E8M0 block scales [rows][K/32]
   uint8_t* out8;            // up: h8 [R][I] out
   uint8_t* oscale;          // up: h8's block scales [R][I/32] out
+  // FP16-activation form of the W4A16 up projection only:
+  const int32_t* xexp;      // per token: act holds x * 2^-xexp[t] as FP16
 };
 
 

@@ -183,6 +183,34 @@ moe4_status moe4_expert_up(const moe4_shape* shape, const uint16_t* x, const int
 moe4_status moe4_expert_down(const moe4_shape* shape, const uint16_t* h, const int32_t* offsets,
                              const moe4_w4* w2, uint16_t* y, void* stream);
 
+/* The up projection's matmul form on FP16 activations (prefill is bound by the matrix
+ * units: GB10 bandwidth-budget article, section "Mechanism: decode is bandwidth-bound,
+ * prefill is compute-bound"; the weights stay NVFP4 against 16-bit activations, i.e.
+ * W4A16: PR804 article, section "NVFP4 is neither uniform 4-bit nor all-FP4 compute").
+ * Each activation row is scaled by its own power of two into FP16, where 4-bit weights
+ * times their E4M3 scale dequantise in half the instructions BF16 needs.
+ *
+ * moe4_act_f16: the activation rows in that form.
+ *   x         BF16 [rows][K] in; K a multiple of 8, at most 16384.
+ *   x16       FP16 [rows][K] out: x[t][k] * 2^-xexp[t], rounded to nearest even.
+ *   xexp      int32 [rows] out: the smallest integer for which max_k |x[t][k]| (NaN
+ *             ignored) times 2^-xexp[t] is below 2^15; 0 for a row of zeros.
+ *   x16 holds x exactly wherever |x[t][k]| >= 2^-31 * max_k |x[t][k]| (and BF16
+ *   subnormals excepted); smaller values round to FP16 subnormals or zero.
+ *   rows == 0 does nothing; rows below 2^31; x and x16 16-byte aligned.
+ *
+ * moe4_expert_up_f16: moe4_expert_up on x16 / xexp from moe4_act_f16 of x (rows = T).
+ *   Always the MFMA GEMM form (H a multiple of 256 and I of 128, else
+ *   MOE4_ERR_UNSUPPORTED), whatever the rows per expert. Products and FP32 partial sums
+ *   are those of the BF16 form scaled by 2^-xexp exactly, and the epilogue scales them
+ *   back, so h has moe4_expert_up's bytes whenever x16 holds x exactly (see above).
+ *   Other arguments as for moe4_expert_up. */
+moe4_status moe4_act_f16(int64_t rows, int32_t K, const uint16_t* x, uint16_t* x16, int32_t* xexp,
+                         void* stream);
+moe4_status moe4_expert_up_f16(const moe4_shape* shape, const uint16_t* x16, const int32_t* xexp,
+                               const int32_t* offsets, const int32_t* perm_src, const moe4_w4* w13,
+                               uint16_t* h, void* stream);
+
 /* add_moe_norm (#627, table "Median time per launch" and the Oct 14 comment).
  *   y         BF16 [T*k][H] expert outputs in plan order.
  *   inv       int32 [T*k] from moe4_permute.

@@ -277,3 +277,37 @@ def test_w4a8_checks():
     assert st == E_WS
     assert lib.moe4_layer_w4a8(shape(T=0), None, None, None, None, None, None, None, None, None, None, None,
                                None, None, None, 0, None) == OK
+
+
+def test_f16_activation_checks():
+    """The FP16-activation pre-pass and up GEMM: shape limits, pointer and descriptor
+    checks, and the layer's workspace growing by x16 and xexp where its up projections
+    run on the GEMM, all before any GPU call."""
+    lib = _lib.load()
+    E_ARG, E_UNS, OK = _lib.MOE4_ERR_INVALID_ARG, _lib.MOE4_ERR_UNSUPPORTED, _lib.MOE4_OK
+    w = W4(FAKE, FAKE, FAKE, _lib.MOE4_W4_TILED)
+    # the pre-pass
+    assert lib.moe4_act_f16(4, 20, FAKE, FAKE, FAKE, None) == E_UNS           # K % 8
+    assert lib.moe4_act_f16(4, 16384 + 8, FAKE, FAKE, FAKE, None) == E_UNS    # K > 16384
+    assert lib.moe4_act_f16(-1, 64, FAKE, FAKE, FAKE, None) == E_ARG
+    assert lib.moe4_act_f16(4, 64, FAKE, FAKE, None, None) == E_ARG
+    assert lib.moe4_act_f16(4, 64, FAKE, FAKE, FAKE + 2, None) == E_ARG       # xexp alignment
+    assert lib.moe4_act_f16(4, 64, FAKE, FAKE + 8, FAKE, None) == E_ARG       # x16 alignment
+    assert lib.moe4_act_f16(1 << 31, 64, FAKE, FAKE, FAKE, None) == E_UNS
+    assert lib.moe4_act_f16(0, 64, None, None, None, None) == OK
+    # the GEMM
+    s = shape(T=8192, H=4096, E=128, I=1536)
+    assert lib.moe4_expert_up_f16(shape(H=2048 + 128), FAKE, FAKE, FAKE, FAKE, w, FAKE, None) == E_UNS
+    assert lib.moe4_expert_up_f16(s, FAKE, FAKE, FAKE, None, w, FAKE, None) == E_ARG
+    assert lib.moe4_expert_up_f16(s, FAKE, None, FAKE, FAKE, w, FAKE, None) == E_ARG
+    assert lib.moe4_expert_up_f16(s, FAKE, FAKE, FAKE, FAKE, W4(FAKE, FAKE, FAKE, 0), FAKE, None) == E_ARG
+    assert lib.moe4_expert_up_f16(s, FAKE, FAKE, FAKE, FAKE, w, None, None) == E_ARG
+    assert lib.moe4_expert_up_f16(shape(T=0), None, None, None, None, None, None, None) == OK
+    # the layer's workspace: x16 [T][H] and xexp [T] on top of the BF16 form's needs
+    # where the up projection runs on the GEMM (40 routed rows per expert on average)
+    pre = shape(T=8192, H=4096, E=128, I=1536)
+    pairs, T, H, I, E = 8192 * 8, 8192, 4096, 1536, 128
+    need = lib.moe4_layer_workspace_bytes(pre)
+    assert need >= (E + 1) * 4 + 2 * pairs * 4 + pairs * (I + H) * 2 + T * H * 2 + T * 4
+    dec = shape()  # decode: no GEMM, no FP16 copy
+    assert lib.moe4_layer_workspace_bytes(dec) < 8 * 2048 * 2 + 64 * (768 + 2048) * 2 + (1 << 20)

@@ -195,8 +195,9 @@ moe4_status moe4_expert_down(const moe4_shape* shape, const uint16_t* h, const i
  *   x16       FP16 [rows][K] out: x[t][k] * 2^-xexp[t], rounded to nearest even.
  *   xexp      int32 [rows] out: the smallest integer for which max_k |x[t][k]| (NaN
  *             ignored) times 2^-xexp[t] is below 2^15; 0 for a row of zeros.
- *   x16 holds x exactly wherever |x[t][k]| >= 2^-31 * max_k |x[t][k]| (and BF16
- *   subnormals excepted); smaller values round to FP16 subnormals or zero.
+ *   x16 holds x exactly wherever |x[t][k]| >= 2^-31 * max_k |x[t][k]|; smaller values
+ *   round to FP16 subnormals or zero. x must be finite (an infinite value leaves the
+ *   row's exponent unspecified).
  *   rows == 0 does nothing; rows below 2^31; x and x16 16-byte aligned.
  *
  * moe4_expert_up_f16: moe4_expert_up on x16 / xexp from moe4_act_f16 of x (rows = T).

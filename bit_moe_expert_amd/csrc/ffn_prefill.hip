@@ -19,9 +19,9 @@
 // half the LDS bytes per flop of 128 x 64 wave tiles that take both operands from LDS.
 // For the up projection the 64 weight rows are 32 gate rows and the matching 32 up
 // rows, so gate and up accumulators of the same h columns sit in the same lanes and
-// SwiGLU is applied in registers. An expert's last tile, when it has at most 192 (or
-// 128) rows, is computed as 6 x 2 (or 4 x 2) blocks a wave, and the activation rows
-// past 192 (or 128) are neither loaded nor computed.
+// SwiGLU is applied in registers. A tile of fewer rows (an expert's last) is computed
+// as MI x 2 blocks a wave, MI = its rows rounded up to 32 (4 to 8), and the activation
+// rows past 32 MI are neither loaded nor computed.
 //
 // Pipeline. Every load is a direct-to-LDS copy (global_load_lds), issued two K steps
 // ahead into a ring of three LDS slots: the activation rows of the tile (gathered
@@ -141,7 +141,7 @@ __device__ __forceinline__ void prefill_gemm(const GemmArgs& a) {
   }
 
   auto compute = [&](auto MIC) {
-    constexpr int MI = decltype(MIC)::value;  // 32-row blocks of the tile: 8, 6 or 4
+    constexpr int MI = decltype(MIC)::value;  // 32-row blocks of the tile: 4 to 8
     constexpr int RW = 8 * MI;                // activation rows each wave copies
     // ---- activations: rows of the tile straight into LDS (global_load_lds) ----
     // Wave w copies LDS rows RW*w .. RW*w + RW-1, 8 rows (1 KB) per instruction: lane l
@@ -315,7 +315,7 @@ __device__ __forceinline__ void prefill_gemm(const GemmArgs& a) {
           // the next step's reads first (the weight bytes, whose dequantisation waits
           // for them, then the activation fragments), the dequantisation after them
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4 + (MI & 1), 0);
 #pragma unroll
           for (int g2 = 0; g2 < MI / 2; ++g2) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -399,8 +399,12 @@ __device__ __forceinline__ void prefill_gemm(const GemmArgs& a) {
             *reinterpret_cast<const u32x4*>(stage + lr * W + lc);
     }
   };
-  if (rows <= BM / 2) compute(std::integral_constant<int, 4>{});
-  else if (rows <= kTq) compute(std::integral_constant<int, 6>{});
+  // 32-row blocks a wave computes: the tile's rows rounded up to 32, from 4 (the
+  // schedule's half tiles) to 8 (only the copies and MFMAs of those rows run)
+  if (rows <= 128) compute(std::integral_constant<int, 4>{});
+  else if (rows <= 160) compute(std::integral_constant<int, 5>{});
+  else if (rows <= 192) compute(std::integral_constant<int, 6>{});
+  else if (rows <= 224) compute(std::integral_constant<int, 7>{});
   else compute(std::integral_constant<int, 8>{});
 }
 

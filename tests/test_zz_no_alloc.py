@@ -41,6 +41,11 @@ CASES = [
      [64, 5]),
     ("decode", wl.workload("decode_t8"), [8, 1]),
     ("batched_t256", wl.workload("batched_t256"), [256, 40]),
+    # enough rows per expert for the GEMM: the up projections run on FP16 activation
+    # rows, which the scratch holds too (the second call still on the GEMM, the third
+    # back on the streaming kernels)
+    ("gemm_f16", wl.Workload("gemm_f16", T=1024, H=1024, E=8, k=2, I=256, routing="zipf", n_shared=1),
+     [1024, 600, 24]),
 ]
 
 

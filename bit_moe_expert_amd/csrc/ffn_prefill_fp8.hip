@@ -329,12 +329,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_fp8_kernel(GemmArgs a
     uint16_t* stage = reinterpret_cast<uint16_t*>((wv < 2 ? lds0 : lds1) + (wv & 1) * 16384);
     const size_t ld = kUp ? a.I : a.N;
     const int col0 = kUp ? nt * 128 + 32 * wv : nt * BN + 64 * wv;
-    constexpr int kHalves = kUp ? 1 : 2;  // down: 128 rows of 64 columns at a time
-    constexpr int HR = 32 * MI / kHalves;   // rows per half
+    constexpr int kHalves = kUp ? 1 : 2;  // down: at most 128 rows of 64 columns at a time
+    constexpr int B0 = (MI + kHalves - 1) / kHalves;  // 32-row blocks of the first half
+    constexpr int HR = 32 * B0;                        // rows of the first half
 #pragma unroll
     for (int half = 0; half < kHalves; ++half) {
 #pragma unroll
-      for (int i = half * MI / kHalves; i < (half + 1) * MI / kHalves; ++i) {
+      for (int i = half * B0; i < (half == 0 ? B0 : MI); ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int lr = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3) - half * HR;
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_fp8_kernel(GemmArgs a
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       if (a.out != nullptr) {  // BF16 rows (y for down; h for up when asked for)
-        constexpr int kPieces = HR * W / 8;
+        const int kPieces = 32 * (half == 0 ? B0 : MI - B0) * W / 8;  // a multiple of 64
 #pragma unroll
         for (int c = 0; c < kPieces / 64; ++c) {
           const int piece = 64 * c + lane, lr = piece / (W / 8), lc = (piece % (W / 8)) * 8;
@@ -384,8 +385,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_fp8_kernel(GemmArgs a
       }
     }
   };
-  if (rows <= BM / 2) compute(std::integral_constant<int, 4>{});
-  else if (rows <= kTq) compute(std::integral_constant<int, 6>{});
+  // 32-row blocks a wave computes: the tile's rows rounded up to 32 (4 to 8)
+  if (rows <= 128) compute(std::integral_constant<int, 4>{});
+  else if (rows <= 160) compute(std::integral_constant<int, 5>{});
+  else if (rows <= 192) compute(std::integral_constant<int, 6>{});
+  else if (rows <= 224) compute(std::integral_constant<int, 7>{});
   else compute(std::integral_constant<int, 8>{});
 }
 

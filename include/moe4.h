@@ -235,7 +235,11 @@ moe4_status moe4_combine_norm(const moe4_shape* shape, const uint16_t* y, const 
  *   topk_idx, topk_w      int32 / FP32 [T][k] out (the routing decision).
  *   residual_out, normed_out  BF16 [T][H] out.
  *   ws                    device workspace of at least moe4_layer_workspace_bytes(shape);
- *                         it holds the plan, h and y between the steps. */
+ *                         it holds the plan, h and y between the steps, and, where the
+ *                         up projections run on the GEMM (40 or more rows per expert on
+ *                         average; T >= 40 for the shared expert), x in moe4_act_f16's
+ *                         form, which those up GEMMs read (same h bytes, see
+ *                         moe4_expert_up_f16). */
 moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_t* w_router,
                        float* logits, const moe4_w4* w13, const moe4_w4* w2,
                        const moe4_w4* shared13, const moe4_w4* shared2,
@@ -245,8 +249,9 @@ moe4_status moe4_layer(const moe4_shape* shape, const uint16_t* x, const uint16_
 
 /* moe4_layer for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same launches,
- * with the plan, h and y in a scratch array of MOE4_NOALLOC_SCRATCH_BYTES that the
- * library holds in each GPU's memory for the life of the process, instead of a
+ * with the plan, h and y (and the FP16 rows) in a scratch array of
+ * MOE4_NOALLOC_SCRATCH_BYTES that the library holds in each GPU's memory for the life
+ * of the process, instead of a
  * caller workspace. Arguments as for moe4_layer, without ws and ws_bytes.
  *   - Shapes whose layer workspace (moe4_layer_workspace_bytes) exceeds
  *     MOE4_NOALLOC_SCRATCH_BYTES return MOE4_ERR_UNSUPPORTED (64 MiB holds decode and

@@ -20,7 +20,7 @@
 // For the up projection the 64 weight rows are 32 gate rows and the matching 32 up
 // rows, so gate and up accumulators of the same h columns sit in the same lanes and
 // SwiGLU is applied in registers. A tile of fewer rows (an expert's last) is computed
-// as MI x 2 blocks a wave, MI = its rows rounded up to 32 (4 to 8), and the activation
+// as MI x 2 blocks a wave, MI = its rows rounded up to 32 (2 to 8), and the activation
 // rows past 32 MI are neither loaded nor computed.
 //
 // Pipeline. Every load is a direct-to-LDS copy (global_load_lds), issued two K steps
@@ -141,7 +141,7 @@ __device__ __forceinline__ void prefill_gemm(const GemmArgs& a) {
   }
 
   auto compute = [&](auto MIC) {
-    constexpr int MI = decltype(MIC)::value;  // 32-row blocks of the tile: 4 to 8
+    constexpr int MI = decltype(MIC)::value;  // 32-row blocks of the tile: 2 to 8
     constexpr int RW = 8 * MI;                // activation rows each wave copies
     // ---- activations: rows of the tile straight into LDS (global_load_lds) ----
     // Wave w copies LDS rows RW*w .. RW*w + RW-1, 8 rows (1 KB) per instruction: lane l
@@ -399,9 +399,11 @@ __device__ __forceinline__ void prefill_gemm(const GemmArgs& a) {
             *reinterpret_cast<const u32x4*>(stage + lr * W + lc);
     }
   };
-  // 32-row blocks a wave computes: the tile's rows rounded up to 32, from 4 (the
-  // schedule's half tiles) to 8 (only the copies and MFMAs of those rows run)
-  if (rows <= 128) compute(std::integral_constant<int, 4>{});
+  // 32-row blocks a wave computes: the tile's rows rounded up to 32, from 2 to 8 (only
+  // the copies and MFMAs of those rows run; the weights are loaded whole whatever MI)
+  if (rows <= 64) compute(std::integral_constant<int, 2>{});
+  else if (rows <= 96) compute(std::integral_constant<int, 3>{});
+  else if (rows <= 128) compute(std::integral_constant<int, 4>{});
   else if (rows <= 160) compute(std::integral_constant<int, 5>{});
   else if (rows <= 192) compute(std::integral_constant<int, 6>{});
   else if (rows <= 224) compute(std::integral_constant<int, 7>{});

@@ -136,7 +136,7 @@ def test_expert_up_f16_same_bits(name, w, layout):
 
 def test_expert_up_f16_tile_edges():
     """Expert groups on the GEMM's tile boundaries (as the BF16 GEMM's tile-edge test)."""
-    counts = [128, 129, 160, 161, 192, 193, 224, 225, 256, 257, 384, 416, 1]
+    counts = [64, 65, 96, 97, 128, 129, 160, 161, 192, 193, 224, 225, 256, 257, 384, 416, 1]
     w = wl.Workload("tile_edges", T=sum(counts), H=512, E=len(counts), k=1, I=256, routing="normal")
     note(f"expert up f16 tile edges: {counts}")
     inp = wl.make_inputs(w, seed=23)
@@ -147,10 +147,10 @@ def test_expert_up_f16_tile_edges():
     assert_bf16_close(oracle.bf16_value(h16), _ref_h(inp, w, off, perm), "h")
 
 
-@pytest.mark.parametrize("T", [40, 77, 150, 220, 300])
+@pytest.mark.parametrize("T", [40, 77, 100, 150, 220, 300])
 def test_expert_up_f16_dense(T):
-    """Dense (shared expert) mode: half tiles, tiles of 5 and 7 blocks of 32 rows, a full
-    tile plus a half one."""
+    """Dense (shared expert) mode: tiles of 2, 3, 4, 5 and 7 blocks of 32 rows, a full
+    tile plus a 2-block one."""
     w = wl.Workload("shared_small", T=T, H=1024, E=1, k=1, I=512, routing="normal")
     note(f"expert up f16 dense T={T}")
     inp = wl.make_inputs(w, seed=22)

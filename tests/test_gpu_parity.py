@@ -298,12 +298,12 @@ def test_expert_ffn_routed(name, w, _):
 
 
 def test_expert_ffn_tile_edges():
-    """Expert groups on the prefill GEMM's tile boundaries: 128 rows (a half tile), 129
-    and 192 (three-quarter tiles, computed as 5 and 6 blocks of 32 rows), 160 and 161
-    (the 5- and 6-block edge), 193 (a full tile with one row in its last quarter, 7
-    blocks), 224 and 225 (the 7- and 8-block edge), 256, 257, 384 (a full tile and a
-    half one), 416 (a full and a three-quarter one) and 1 row."""
-    counts = [128, 129, 160, 161, 192, 193, 224, 225, 256, 257, 384, 416, 1]
+    """Expert groups on the prefill GEMM's tile boundaries: a tile computes its rows
+    rounded up to 32 (2 to 8 blocks of 32 rows a wave), so 64/65, 96/97, 128/129,
+    160/161, 192/193, 224/225 and 256/257 rows sit on the block edges (128 and below
+    are the schedule's half tiles, 129 to 192 its three-quarter ones); 384 (a full tile
+    and a half one), 416 (a full and a three-quarter one) and 1 row."""
+    counts = [64, 65, 96, 97, 128, 129, 160, 161, 192, 193, 224, 225, 256, 257, 384, 416, 1]
     w = wl.Workload("tile_edges", T=sum(counts), H=512, E=len(counts), k=1, I=256, routing="normal")
     note(f"expert ffn tile edges: groups {counts}")
     inp = wl.make_inputs(w, seed=3)
@@ -391,12 +391,12 @@ def test_expert_ffn_signed_block_scales(name):
     _check_routed_ffn(inp, w, off, perm)
 
 
-@pytest.mark.parametrize("T", [1, 8, 17, 39, 77, 150, 200, 220, 300])
+@pytest.mark.parametrize("T", [1, 8, 17, 39, 50, 77, 100, 150, 200, 220, 300])
 def test_expert_ffn_dense_shared(T):
     """Dense (shared expert) mode: on the streaming kernel below 40 rows (1, 8, 17 and
     39 rows: one or several 16-row passes, a ragged last one), and on the prefill GEMM
-    from 40: one half tile (77 rows), tiles of 5, 7 and 8 blocks of 32 rows (150, 200,
-    220) and a full tile plus a half one (300)."""
+    from 40: tiles of 2, 3, 4, 5 and 7 blocks of 32 rows (50, 77, 100, 150, 200, 220)
+    and a full tile plus a 2-block one (300)."""
     w = wl.Workload("shared_small", T=T, H=1024, E=1, k=1, I=512, routing="normal")
     note(f"expert ffn dense (shared expert mode) T={T}")
     inp = wl.make_inputs(w, seed=2)

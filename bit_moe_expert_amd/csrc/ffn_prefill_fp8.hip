@@ -385,8 +385,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_fp8_kernel(GemmArgs a
       }
     }
   };
-  // 32-row blocks a wave computes: the tile's rows rounded up to 32 (4 to 8)
-  if (rows <= 128) compute(std::integral_constant<int, 4>{});
+  // 32-row blocks a wave computes: the tile's rows rounded up to 32 (2 to 8)
+  if (rows <= 64) compute(std::integral_constant<int, 2>{});
+  else if (rows <= 96) compute(std::integral_constant<int, 3>{});
+  else if (rows <= 128) compute(std::integral_constant<int, 4>{});
   else if (rows <= 160) compute(std::integral_constant<int, 5>{});
   else if (rows <= 192) compute(std::integral_constant<int, 6>{});
   else if (rows <= 224) compute(std::integral_constant<int, 7>{});

@@ -184,10 +184,10 @@ def test_expert_ffn_w4a8_routed(name, w):
 
 
 def test_expert_ffn_w4a8_tile_edges():
-    """Expert groups on the GEMM's tile boundaries (as for the W4A16 GEMM: tiles of 4 to
-    8 blocks of 32 rows and their edges at 128/129, 160/161, 192/193, 224/225, 256/257,
-    full tiles with half and three-quarter last ones, 1 row)."""
-    counts = [128, 129, 160, 161, 192, 193, 224, 225, 256, 257, 384, 416, 1]
+    """Expert groups on the GEMM's tile boundaries (as for the W4A16 GEMM: tiles of 2 to
+    8 blocks of 32 rows and their edges at 64/65, 96/97, 128/129, 160/161, 192/193,
+    224/225, 256/257, full tiles with half and three-quarter last ones, 1 row)."""
+    counts = [64, 65, 96, 97, 128, 129, 160, 161, 192, 193, 224, 225, 256, 257, 384, 416, 1]
     w = wl.Workload("tile_edges", T=sum(counts), H=512, E=len(counts), k=1, I=256, routing="normal")
     note(f"w4a8 expert ffn tile edges: groups {counts}")
     inp = wl.make_inputs(w, seed=3)
@@ -258,10 +258,10 @@ def _check_rows_condition(got_h, got_y, x_rows, W13, ts13, W2, ts2, what, eps=2.
     assert np.all(np.abs(got_y - ref_y) <= tol_y), f"y {what}: worst {float(np.max(np.abs(got_y - ref_y) / tol_y)):.2f}x"
 
 
-@pytest.mark.parametrize("T", [1, 77, 150, 220, 300])
+@pytest.mark.parametrize("T", [1, 50, 77, 100, 150, 220, 300])
 def test_expert_ffn_w4a8_dense_shared(T):
-    """Dense (shared expert) mode: one half tile, tiles of 5 and 7 blocks of 32 rows, a
-    full tile plus a half one; T = 1 as the degenerate case."""
+    """Dense (shared expert) mode: tiles of 2, 3, 4, 5 and 7 blocks of 32 rows, a full
+    tile plus a 2-block one; T = 1 as the degenerate case."""
     w = wl.Workload("shared_small", T=T, H=1024, E=1, k=1, I=512, routing="normal")
     note(f"w4a8 expert ffn dense T={T}")
     inp = wl.make_inputs(w, seed=2)
